@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of the LLM.int8() linear layer on one MI355X.
+
+One step = one int8_linear_forward call (outlier detection, masked row
+quantization + gathers, fused int8/fp16 product with epilogue) on the 13B-scale
+first feed-forward layer: X fp16 [2048, 5120] with 6 planted outlier columns,
+W [20480, 5120] held as CB/SCB (quantized once, outside the timed region).
+Inputs are seeded synthetic data resident in HBM before timing starts.
+
+Prints one JSON line: effective TOPS (2*T*N*K per second over the whole
+call), the roofline entry of the dominant kernel (the fused product, timed by
+HIP events the library records around it on the same stream), the fp16
+torch linear on the same shape for comparison, and the CPU oracle timed on a
+bounded sample on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+GEMM_SOURCES = ["int8_mixed_precision_detect_amd/csrc/k_gemm.hip",
+                "int8_mixed_precision_detect_amd/csrc/common.h",
+                "int8_mixed_precision_detect_amd/csrc/kernels.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_13b_traffic.txt")
+
+
+def kernel_fingerprint() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the product kernel from the committed counter
+    summary, or None when it is missing or was taken on other kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_fingerprint") != kernel_fingerprint() or kv.get("workload") != workload:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(d, cols: int):
+    """The oracle as it stands, on all rows and the first `cols` output channels."""
+    import numpy as np
+    import oracle.llm_int8 as O
+    X, W, bias, thr = d["X"], d["W"], d["bias"], d["threshold"]
+    T, K = X.shape
+    CB, SCB = O.quantize_weight(W[:cols])          # load-time step, not timed
+    b = None if bias is None else bias[:cols]
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        O.linear_forward(X, CB, SCB, b, thr)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    return {"value": 2.0 * T * cols * K / t / 1e12, "unit": "TOPS",
+            "cores": threads or cores, "host_cores": cores, "kind": "oracle",
+            "sample": f"full forward of the CPU oracle (NumPy, float64 BLAS) on all {T} rows and "
+                      f"the first {cols} of {W.shape[0]} output channels, median of 3 runs "
+                      f"({t:.2f} s each)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="13b")
+    ap.add_argument("--copies", type=int, default=3,
+                    help="rotate this many copies of X/CB/SCB/Y so the 256 MB last-level "
+                         "cache cannot hold one step's inputs from the step before")
+    ap.add_argument("--cpu-cols", type=int, default=10240)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp16", action="store_true")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1 "
+              f"(got {args.gpus})", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import int8_mixed_precision_detect_amd as i8
+    from workloads import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    T, K, N = wl.T, wl.K, wl.N
+    d = make_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    copies = max(1, args.copies)
+    Xs, CBs, SCBs, Ys = [], [], [], []
+    Wd = torch.from_numpy(d["W"]).to(dev)
+    for _ in range(copies):
+        Xs.append(torch.from_numpy(d["X"]).to(dev))
+        CB, SCB = i8.quantize_weight(Wd)
+        CBs.append(CB)
+        SCBs.append(SCB)
+        Ys.append(torch.empty((T, N), dtype=torch.float16, device=dev))
+    bias = None if d["bias"] is None else torch.from_numpy(d["bias"]).to(dev)
+    ws = i8.alloc_workspace(T, N, K, None, dev)
+    torch.cuda.synchronize()
+
+    def step(s):
+        c = s % copies
+        i8.linear_forward(Xs[c], CBs[c], SCBs[c], bias, wl.threshold, workspace=ws, out=Ys[c])
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    code, n_o = i8.linear_status(ws)
+    if code != 0:
+        raise RuntimeError(f"forward reported status {code}")
+
+    i8.profile_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(s)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    stage_ms, calls = i8.profile_read()
+    i8.profile_enable(False)
+    ms_per_step = ms_total / args.steps
+    stage_avg = [m / max(calls, 1) for m in stage_ms]
+
+    ops = 2.0 * T * N * K
+    tops = ops / (ms_per_step * 1e-3) / 1e12
+    gemm_ms = stage_avg[2]
+    achieved = ops / (gemm_ms * 1e-3) / 1e12
+    traffic = read_traffic(args.workload)
+    n_pad = -(-n_o // 32) * 32
+    detect_bytes = 2.0 * T * K
+    quant_bytes = 2.0 * T * K + N * n_o + T * K + 4 * T + 2 * T * n_pad + 2 * N * n_pad
+
+    result = {
+        "metric": "effective TOPS (2TNK/s) of int8_linear_forward at T=2048; % int8 MFMA peak",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}-scale first FF layer (LLM.int8() linear)",
+                   "T": T, "K": K, "N": N, "threshold": wl.threshold, "n_outliers": n_o,
+                   "bias": d["bias"] is not None, "buffer_copies": copies},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic, "kernel": "k_gemm (fused int8 product + epilogue)",
+                     "avg_ms": round(gemm_ms, 5), "algorithmic_ops_per_launch": ops},
+        "stages_ms": {"detect": round(stage_avg[0], 5), "quantize_gather": round(stage_avg[1], 5),
+                      "product": round(stage_avg[2], 5), "whole_call": round(stage_avg[3], 5)},
+        "stages_hbm_frac": {
+            "detect": round(detect_bytes / (stage_avg[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "quantize_gather": round(quant_bytes / (stage_avg[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "pct_int8_peak_whole_call": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+    }
+
+    if not args.no_fp16:
+        Wh = Wd
+        Xh = Xs[0]
+        F = torch.nn.functional
+        for _ in range(5):
+            F.linear(Xh, Wh, bias)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = max(10, args.steps // 2)
+        e0.record()
+        for _ in range(reps):
+            F.linear(Xh, Wh, bias)
+        e1.record()
+        torch.cuda.synchronize()
+        fp16_ms = e0.elapsed_time(e1) / reps
+        result["fp16_linear"] = {"ms": round(fp16_ms, 5),
+                                 "tflops": round(ops / (fp16_ms * 1e-3) / 1e12, 2),
+                                 "int8_over_fp16_time": round(ms_per_step / fp16_ms, 4)}
+
+    if args.copy_calib_mb > 0:
+        nbytes = args.copy_calib_mb << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = nbytes
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d, min(args.cpu_cols, N))
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,214 @@
+/*
+ * i8mm.h -- C ABI of libi8mm, an MI355X (gfx950) implementation of the
+ * LLM.int8() mixed-precision linear layer  Y = X . W^T + b.
+ *
+ * The method, as the pages describe it:
+ *   Hugging Face "LLM.int8() を Transformers と Accelerate に統合" summary
+ *   (agentlenshq.com), section "LLM.int8() の核心アイデア", steps 1-3:
+ *   (1) the hidden dims of X (columns) holding a value of magnitude above a
+ *       threshold (~6) are outliers;
+ *   (2) outlier columns are multiplied in fp16, the rest is quantized
+ *       vector-wise (one absmax scale per row of X, one per output channel
+ *       of W) and multiplied in int8;
+ *   (3) the int8 result is dequantized and added to the fp16 result.
+ *   Absmax quantization: section "量子化の仕組み" (divide by the absmax,
+ *   multiply by 127, round; codes in [-127, 127]).  The weight is stored as
+ *   int8 CB plus a scale SCB with W ~= CB * SCB / 127: section
+ *   "transformers への統合".  The split also takes the matching weight dims:
+ *   zenn.dev LLM.int8() summary, section "手法".
+ *
+ * Conventions that hold for every entry point:
+ *   - All tensor arguments are DEVICE pointers (memory of the GPU that is
+ *     current when the call is made), owned by the caller.  The library
+ *     never allocates, frees or keeps them.
+ *   - fp16 means IEEE binary16 (_Float16 / torch.float16); every tensor is
+ *     row-major and dense unless a leading dimension (ld*) is given, in
+ *     elements.
+ *   - Every call only validates arguments on the host and enqueues kernels
+ *     on `stream` (NULL = the default stream).  It does not synchronize,
+ *     except int8_linear_status, which says so.  Results are ready when the
+ *     stream has reached that point.
+ *   - The return value reports host-detectable errors and launch failures
+ *     (I8MM_ERR_HIP, from hipGetLastError after the launches).  Errors found
+ *     on the device (more outliers than max_outliers) are reported through
+ *     the workspace and read back with int8_linear_status.
+ *   - Quantized codes use round-half-away-from-zero of the IEEE fp32
+ *     quotient fl32(x * 127) / s; a zero scale gives code 0.  Codes are in
+ *     [-127, 127]; -128 never appears.
+ *   - Activations must be finite; non-finite inputs give undefined results.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef I8MM_H
+#define I8MM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define I8MM_ABI_VERSION 1
+
+typedef enum {
+  I8MM_OK = 0,
+  I8MM_ERR_INVALID_ARG = 1,     /* null pointer, negative size, bad threshold, misalignment */
+  I8MM_ERR_WORKSPACE = 2,       /* ws_bytes smaller than the size query returns */
+  I8MM_ERR_UNSUPPORTED = 3,     /* shape the library cannot handle (sizes above 2^31-1) */
+  I8MM_ERR_HIP = 4,             /* a HIP runtime call or kernel launch failed */
+  I8MM_ERR_OUTLIER_OVERFLOW = 5 /* device found more outlier columns than max_outliers */
+} i8mm_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* i8mm_status_string(i8mm_status s);
+
+/* I8MM_ABI_VERSION of the built library. */
+int i8mm_abi_version(void);
+
+/*
+ * Weight quantization (done once per weight, when it is moved to the GPU;
+ * "transformers への統合" section of the Hugging Face summary).
+ *
+ *   SCB[j]   = max_k |W[j,k]|                      (fp32, exact)
+ *   CB[j,k]  = rhaz(fl32(W[j,k] * 127) / SCB[j])   (0 when SCB[j] == 0)
+ *
+ * so that W ~= CB * SCB / 127 with |W - CB*SCB/127| <= SCB/254.
+ *   W   : fp16 [N, K], nn.Linear layout (row j = output channel j)
+ *   CB  : int8 [N, K] out
+ *   SCB : fp32 [N]    out
+ * N, K >= 0 (K == 0 gives SCB = 0).  W must be 2-byte aligned.
+ */
+i8mm_status int8_quantize_weight(const void* W, int64_t N, int64_t K,
+                                 int8_t* CB, float* SCB, hipStream_t stream);
+
+/*
+ * Workspace of int8_linear_forward.  Every region starts on a 256-byte
+ * boundary of `ws`; offsets are in bytes from `ws`.
+ */
+typedef struct {
+  size_t counts;   /* int32[4]: n_o (true count), overflow flag, 0, 0          */
+  size_t outliers; /* int32[max_outliers]: outlier columns O, ascending       */
+  size_t mask;     /* uint32[ceil(K/32)]: bit k set iff column k is an outlier */
+  size_t partial;  /* uint32[n_row_blocks][ceil(K/32)]: per-row-block flags    */
+  size_t sx;       /* fp32[T]: row scales (absmax over non-outlier columns)    */
+  size_t xq;       /* int8[T][ldq]: quantized X, outlier and pad columns 0     */
+  size_t xo;       /* fp16[T][ldo]: X[:, O], zero-padded to ldo                */
+  size_t wo;       /* fp16[N][ldo]: fp16(CB[:, O] * SCB / 127), zero-padded    */
+  int64_t ldq;     /* row pitch of xq in bytes (K rounded up to 64)            */
+  int64_t ldo;     /* row pitch of xo and wo in elements (max_outliers up to 32) */
+  int64_t n_row_blocks;
+  size_t total;    /* bytes the workspace must hold                            */
+} i8mm_ws_layout;
+
+/* Fill *out for a forward call of this shape.  max_outliers in [0, K]. */
+i8mm_status int8_linear_workspace_layout(int64_t T, int64_t N, int64_t K,
+                                         int64_t max_outliers, i8mm_ws_layout* out);
+
+/* out->total of the layout above (0 on invalid arguments). */
+size_t int8_linear_workspace_size(int64_t T, int64_t N, int64_t K, int64_t max_outliers);
+
+/*
+ * The layer (steps 1-3 of "LLM.int8() の核心アイデア"):
+ *
+ *   O      = ascending { k : exists i, |X[i,k]| >= threshold }
+ *   sx[i]  = max_{k not in O} |X[i,k]|
+ *   Xq     = rhaz(fl32(X * 127) / sx[i]) on columns not in O, 0 on O
+ *   acc    = Xq . CB^T                                   (exact, int32)
+ *   Wo     = fp16(fl32(fl32(CB[:,O] * SCB[j]) / 127))
+ *   Y[i,j] = fp16( acc*sx[i]*SCB[j]/127^2 + sum_o X[i,O_o]*Wo[j,o] + bias[j] )
+ *            (fp32 arithmetic, one final round-to-nearest-even)
+ *
+ *   X        : fp16 [T, K]
+ *   CB, SCB  : from int8_quantize_weight, [N, K] and [N]
+ *   bias     : fp16 [N], or NULL for no bias
+ *   threshold: > 0; +inf means no column is an outlier (plain vector-wise
+ *              int8).  NaN or <= 0 -> I8MM_ERR_INVALID_ARG.
+ *   Y        : fp16 [T, N] out; must not overlap X, CB or the workspace
+ *   ws       : device workspace, 256-byte aligned, ws_bytes >=
+ *              int8_linear_workspace_size(T, N, K, max_outliers); its
+ *              regions hold the intermediate results after the call
+ *              (see i8mm_ws_layout)
+ *   max_outliers: capacity of O, in [0, K]; K is always enough.  If the
+ *              device finds more, Y is undefined and int8_linear_status
+ *              returns I8MM_ERR_OUTLIER_OVERFLOW; no memory outside the
+ *              arguments is touched.
+ * T, N, K >= 0; T == 0 or N == 0 is a no-op; K == 0 gives Y = bias (or 0).
+ */
+i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K,
+                                const int8_t* CB, const float* SCB, int64_t N,
+                                const void* bias, float threshold, void* Y,
+                                void* ws, size_t ws_bytes, int64_t max_outliers,
+                                hipStream_t stream);
+
+/*
+ * Synchronizes `stream`, then reads the counts of the last forward call that
+ * used `ws`: *n_outliers = number of outlier columns found (may exceed
+ * max_outliers).  Returns I8MM_ERR_OUTLIER_OVERFLOW if it did, else I8MM_OK.
+ * n_outliers may be NULL.
+ */
+i8mm_status int8_linear_status(const void* ws, int32_t* n_outliers, hipStream_t stream);
+
+/* ---- stage entry points (the same kernels the forward runs) -------------- */
+
+/*
+ * Step 1 alone.  Writes counts[0] = n_o, counts[1] = overflow (n_o >
+ * max_outliers), O[0 .. min(n_o, max_outliers)) ascending, and the bit mask
+ * mask[ceil(K/32)] (bit k%32 of word k/32).  `partial` is scratch of
+ * int8_find_outliers_scratch_size(T, K) bytes.  counts: int32[4].
+ */
+size_t int8_find_outliers_scratch_size(int64_t T, int64_t K);
+i8mm_status int8_find_outliers(const void* X, int64_t T, int64_t K, float threshold,
+                               int32_t* O, int32_t* counts, uint32_t* mask,
+                               int64_t max_outliers, void* partial, size_t partial_bytes,
+                               hipStream_t stream);
+
+/*
+ * Step 2, activation side, for a given outlier set (O ascending, counts[0] =
+ * n_o, only the first min(n_o, max_outliers) entries are read):
+ *   sx[T], Xq[T][ldq] (ldq >= K bytes, multiple of 16; columns K..ldq-1 and
+ *   outlier columns written as 0), Xo[T][ldo] fp16 = X[:, O] with columns
+ *   n_o..roundup(n_o,32)-1 written as 0 (ldo multiple of 32, ldo >=
+ *   roundup(min(n_o, max_outliers), 32)).
+ * mask may be NULL (then it is rebuilt from O inside the kernel).
+ */
+i8mm_status int8_quantize_rows(const void* X, int64_t T, int64_t K,
+                               const int32_t* O, const int32_t* counts, const uint32_t* mask,
+                               int64_t max_outliers, int8_t* Xq, int64_t ldq, float* sx,
+                               void* Xo, int64_t ldo, hipStream_t stream);
+
+/*
+ * Step 2, weight side: Wo[N][ldo] fp16, Wo[j,o] = fp16(fl32(fl32(CB[j,O[o]] *
+ * SCB[j]) / 127)) for o < n_o, 0 for n_o <= o < roundup(n_o, 32).
+ */
+i8mm_status int8_outlier_weights(const int8_t* CB, const float* SCB, int64_t N, int64_t K,
+                                 const int32_t* O, const int32_t* counts, int64_t max_outliers,
+                                 void* Wo, int64_t ldo, hipStream_t stream);
+
+/*
+ * The int8 product of step 2 with its int32 accumulators written out:
+ *   C[i,j] = sum_k A[i,k] * B[j,k]   (exact; caller keeps K*127^2 < 2^31)
+ *   A: int8 [T][lda], B: int8 [N][ldb], C: int32 [T][N].  lda, ldb >= K.
+ */
+i8mm_status int8_gemm_s32(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
+                          int32_t* C, int64_t T, int64_t N, int64_t K, hipStream_t stream);
+
+/* ---- instrumentation ------------------------------------------------------ */
+
+/*
+ * When enabled, every int8_linear_forward call records HIP events on its
+ * stream around its stages: 0 = detect (step 1), 1 = quantize and gather
+ * (step 2 prep), 2 = the fused int8/fp16 product and epilogue, 3 = the whole
+ * call.  i8mm_profile_read synchronizes those events and returns, per stage,
+ * the summed milliseconds and the number of calls timed since the last
+ * enable (arrays of 4; either pointer may be NULL).  At most 4096 calls are
+ * kept; later calls are not timed.
+ */
+i8mm_status i8mm_profile_enable(int on);
+i8mm_status i8mm_profile_read(double* ms_sum, int64_t* calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I8MM_H */

@@ -1,0 +1,214 @@
+"""LLM.int8() mixed-precision linear layer for MI355X (gfx950).
+
+A thin binding over libi8mm's C ABI (include/i8mm.h): it checks tensor
+dtypes, devices and contiguity, allocates outputs and the workspace with
+torch, and passes raw device pointers and torch's current HIP stream.  All
+arithmetic happens in the library's HIP kernels; there is no CPU path.
+
+The method (Hugging Face LLM.int8() summary, section "LLM.int8() の核心アイデア"):
+outlier hidden dims (columns of X with some |x| >= threshold) are multiplied
+in fp16, the rest is absmax-quantized to int8 (per row of X, per output
+channel of W) and multiplied with int32 accumulation, then dequantized and
+summed with the fp16 part.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import I8mmError, WsLayout, check, lib
+
+__all__ = [
+    "I8mmError", "quantize_weight", "linear_forward", "workspace_layout", "workspace_size",
+    "alloc_workspace", "linear_status", "find_outliers", "quantize_rows", "outlier_weights",
+    "gemm_s32", "profile_enable", "profile_read", "Int8Linear",
+]
+
+DEFAULT_THRESHOLD = 6.0
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quantize_weight(W: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fp16 W [N,K] -> (CB int8 [N,K], SCB fp32 [N]) with W ~= CB*SCB/127."""
+    _need(W, "W", torch.float16, 2)
+    N, K = W.shape
+    CB = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    SCB = torch.empty((N,), dtype=torch.float32, device=W.device)
+    check("int8_quantize_weight",
+          lib().int8_quantize_weight(_ptr(W), N, K, _ptr(CB), _ptr(SCB), _stream(W)))
+    return CB, SCB
+
+
+def workspace_layout(T: int, N: int, K: int, max_outliers: Optional[int] = None) -> dict:
+    mo = K if max_outliers is None else max_outliers
+    L = WsLayout()
+    check("int8_linear_workspace_layout",
+          lib().int8_linear_workspace_layout(T, N, K, mo, ctypes.byref(L)))
+    return {f: getattr(L, f) for f, _ in WsLayout._fields_}
+
+
+def workspace_size(T: int, N: int, K: int, max_outliers: Optional[int] = None) -> int:
+    return workspace_layout(T, N, K, max_outliers)["total"]
+
+
+def alloc_workspace(T: int, N: int, K: int, max_outliers: Optional[int] = None,
+                    device="cuda") -> torch.Tensor:
+    """A uint8 device buffer big enough for a forward call of this shape."""
+    return torch.empty(max(workspace_size(T, N, K, max_outliers), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def linear_forward(X: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor,
+                   bias: Optional[torch.Tensor] = None, threshold: float = DEFAULT_THRESHOLD,
+                   max_outliers: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y fp16 [T,N] = the LLM.int8() product of X fp16 [T,K] with (CB, SCB), plus bias."""
+    _need(X, "X", torch.float16, 2)
+    _need(CB, "CB", torch.int8, 2)
+    _need(SCB, "SCB", torch.float32, 1)
+    T, K = X.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or SCB.shape[0] != N:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)} CB {tuple(CB.shape)} "
+                         f"SCB {tuple(SCB.shape)}")
+    if bias is not None:
+        _need(bias, "bias", torch.float16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias must have N elements")
+    mo = K if max_outliers is None else max_outliers
+    if workspace is None:
+        workspace = alloc_workspace(T, N, K, mo, X.device)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=X.device)
+    else:
+        _need(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (T, N):
+            raise ValueError("out must be [T, N]")
+    check("int8_linear_forward",
+          lib().int8_linear_forward(_ptr(X), T, K, _ptr(CB), _ptr(SCB), N, _ptr(bias),
+                                    float(threshold), _ptr(out), _ptr(workspace),
+                                    workspace.numel(), mo, _stream(X)))
+    return out
+
+
+def linear_status(workspace: torch.Tensor) -> Tuple[int, int]:
+    """(status code, n_outliers) of the last forward call on this workspace (syncs)."""
+    n = ctypes.c_int32(0)
+    code = lib().int8_linear_status(_ptr(workspace), ctypes.byref(n), _stream(workspace))
+    return code, n.value
+
+
+def find_outliers(X: torch.Tensor, threshold: float = DEFAULT_THRESHOLD,
+                  max_outliers: Optional[int] = None):
+    """Step 1 alone: (O int32 [max_outliers], counts int32 [4], mask uint32-as-int32)."""
+    _need(X, "X", torch.float16, 2)
+    T, K = X.shape
+    mo = K if max_outliers is None else max_outliers
+    O = torch.empty(max(mo, 1), dtype=torch.int32, device=X.device)
+    counts = torch.empty(4, dtype=torch.int32, device=X.device)
+    mask = torch.empty(max((K + 31) // 32, 1), dtype=torch.int32, device=X.device)
+    nbytes = lib().int8_find_outliers_scratch_size(T, K)
+    part = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=X.device)
+    check("int8_find_outliers",
+          lib().int8_find_outliers(_ptr(X), T, K, float(threshold), _ptr(O), _ptr(counts),
+                                   _ptr(mask), mo, _ptr(part), part.numel(), _stream(X)))
+    return O, counts, mask
+
+
+def quantize_rows(X: torch.Tensor, O: torch.Tensor, counts: torch.Tensor,
+                  max_outliers: int, mask: Optional[torch.Tensor] = None,
+                  ldq: Optional[int] = None, ldo: Optional[int] = None):
+    """Step 2, activation side: (Xq int8 [T,ldq], sx fp32 [T], Xo fp16 [T,ldo])."""
+    _need(X, "X", torch.float16, 2)
+    T, K = X.shape
+    ldq = ((K + 63) // 64) * 64 if ldq is None else ldq
+    ldo = max(((max_outliers + 31) // 32) * 32, 32) if ldo is None else ldo
+    Xq = torch.empty((T, ldq), dtype=torch.int8, device=X.device)
+    sx = torch.empty(T, dtype=torch.float32, device=X.device)
+    Xo = torch.empty((T, ldo), dtype=torch.float16, device=X.device)
+    check("int8_quantize_rows",
+          lib().int8_quantize_rows(_ptr(X), T, K, _ptr(O), _ptr(counts), _ptr(mask), max_outliers,
+                                   _ptr(Xq), ldq, _ptr(sx), _ptr(Xo), ldo, _stream(X)))
+    return Xq, sx, Xo
+
+
+def outlier_weights(CB: torch.Tensor, SCB: torch.Tensor, O: torch.Tensor, counts: torch.Tensor,
+                    max_outliers: int, ldo: Optional[int] = None) -> torch.Tensor:
+    """Step 2, weight side: Wo fp16 [N, ldo] = fp16(CB[:, O] * SCB / 127), zero-padded."""
+    _need(CB, "CB", torch.int8, 2)
+    N, K = CB.shape
+    ldo = max(((max_outliers + 31) // 32) * 32, 32) if ldo is None else ldo
+    Wo = torch.empty((N, ldo), dtype=torch.float16, device=CB.device)
+    check("int8_outlier_weights",
+          lib().int8_outlier_weights(_ptr(CB), _ptr(SCB), N, K, _ptr(O), _ptr(counts),
+                                     max_outliers, _ptr(Wo), ldo, _stream(CB)))
+    return Wo
+
+
+def gemm_s32(A: torch.Tensor, B: torch.Tensor, K: Optional[int] = None) -> torch.Tensor:
+    """C int32 [T,N] = A int8 [T,>=K] . B int8 [N,>=K]^T over the first K columns."""
+    _need(A, "A", torch.int8, 2)
+    _need(B, "B", torch.int8, 2)
+    T, N = A.shape[0], B.shape[0]
+    K = A.shape[1] if K is None else K
+    C = torch.empty((T, N), dtype=torch.int32, device=A.device)
+    check("int8_gemm_s32",
+          lib().int8_gemm_s32(_ptr(A), A.shape[1], _ptr(B), B.shape[1], _ptr(C), T, N, K,
+                              _stream(A)))
+    return C
+
+
+def profile_enable(on: bool = True) -> None:
+    check("i8mm_profile_enable", lib().i8mm_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """(ms per stage summed [detect, quantize, product, whole], calls timed)."""
+    ms = (ctypes.c_double * 4)()
+    calls = (ctypes.c_int64 * 4)()
+    check("i8mm_profile_read", lib().i8mm_profile_read(ms, calls))
+    return list(ms), int(calls[3])
+
+
+class Int8Linear:
+    """A linear layer holding its weight as CB/SCB (the pages' ``Linear8bitLt``
+    with ``has_fp16_weights=False``): quantize once, then call."""
+
+    def __init__(self, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                 threshold: float = DEFAULT_THRESHOLD):
+        self.CB, self.SCB = quantize_weight(weight.contiguous())
+        self.bias = None if bias is None else bias.contiguous()
+        self.threshold = threshold
+        self._ws = None
+        self._ws_key = None
+
+    def __call__(self, X: torch.Tensor) -> torch.Tensor:
+        T, K = X.shape
+        key = (T, X.device)
+        if self._ws_key != key:
+            self._ws = alloc_workspace(T, self.CB.shape[0], K, None, X.device)
+            self._ws_key = key
+        return linear_forward(X.contiguous(), self.CB, self.SCB, self.bias, self.threshold,
+                              workspace=self._ws)

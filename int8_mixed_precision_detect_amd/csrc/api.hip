@@ -1,0 +1,304 @@
+// Host side of the libi8mm C ABI: argument checks, workspace carving and
+// kernel sequencing on the caller's stream.  See include/i8mm.h for the
+// contract of every entry point.
+#include <math.h>
+#include <mutex>
+#include <vector>
+
+#include "../../include/i8mm.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace i8mm;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // sizes must fit int32 indexing of O
+constexpr int64_t kMaxK = (int64_t)1 << 18;    // LDS copy of the outlier bit mask (32 KB)
+
+inline bool aligned(const void* p, uintptr_t a) { return (((uintptr_t)p) & (a - 1)) == 0; }
+
+struct DetectGeom {
+  int64_t rows_per_block, nrb;
+};
+
+// Row blocks of the detection pass: aim at >= 2048 workgroups, at least 16
+// rows (4 per wave) per workgroup, and a grid.y that HIP accepts.
+DetectGeom detect_geom(int64_t T, int64_t K) {
+  const int64_t slabs = ceil_div(K > 0 ? K : 1, 512);
+  const int64_t want = ceil_div(2048, slabs);
+  int64_t rpb = round_up(ceil_div(T > 0 ? T : 1, want), 8);
+  if (rpb < 16) rpb = 16;
+  while (ceil_div(T, rpb) > 65535) rpb *= 2;
+  return {rpb, ceil_div(T > 0 ? T : 1, rpb)};
+}
+
+i8mm_status layout_of(int64_t T, int64_t N, int64_t K, int64_t max_o, i8mm_ws_layout* L) {
+  if (T < 0 || N < 0 || K < 0 || max_o < 0 || max_o > K) return I8MM_ERR_INVALID_ARG;
+  if (T >= kMaxDim || N >= kMaxDim || K > kMaxK) return I8MM_ERR_UNSUPPORTED;
+  const DetectGeom g = detect_geom(T, K);
+  const int64_t KW = ceil_div(K, 32);
+  L->ldq = round_up(K, 64);
+  L->ldo = round_up(max_o, 32);
+  L->n_row_blocks = g.nrb;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (size_t)round_up((int64_t)(off + bytes), kAlign);
+    return o;
+  };
+  L->counts = take(16);
+  L->outliers = take((size_t)(max_o > 0 ? max_o : 1) * 4);
+  L->mask = take((size_t)(KW > 0 ? KW : 1) * 4);
+  L->partial = take((size_t)(g.nrb * (KW > 0 ? KW : 1)) * 4);
+  L->sx = take((size_t)T * 4);
+  L->xq = take((size_t)T * (size_t)L->ldq);
+  L->xo = take((size_t)T * (size_t)L->ldo * 2);
+  L->wo = take((size_t)N * (size_t)L->ldo * 2);
+  L->total = off;
+  return I8MM_OK;
+}
+
+i8mm_status hip_status() {
+  return hipGetLastError() == hipSuccess ? I8MM_OK : I8MM_ERR_HIP;
+}
+
+// ---- instrumentation state ----
+constexpr int kProfCap = 4096;
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+int g_prof_n = 0;
+std::vector<hipEvent_t> g_prof_ev;  // kProfCap * 4 events, created on first enable
+
+}  // namespace
+
+extern "C" {
+
+const char* i8mm_status_string(i8mm_status s) {
+  switch (s) {
+    case I8MM_OK: return "I8MM_OK";
+    case I8MM_ERR_INVALID_ARG: return "I8MM_ERR_INVALID_ARG";
+    case I8MM_ERR_WORKSPACE: return "I8MM_ERR_WORKSPACE";
+    case I8MM_ERR_UNSUPPORTED: return "I8MM_ERR_UNSUPPORTED";
+    case I8MM_ERR_HIP: return "I8MM_ERR_HIP";
+    case I8MM_ERR_OUTLIER_OVERFLOW: return "I8MM_ERR_OUTLIER_OVERFLOW";
+  }
+  return "I8MM_UNKNOWN_STATUS";
+}
+
+int i8mm_abi_version(void) { return I8MM_ABI_VERSION; }
+
+i8mm_status int8_quantize_weight(const void* W, int64_t N, int64_t K, int8_t* CB, float* SCB,
+                                 hipStream_t stream) {
+  if (N < 0 || K < 0) return I8MM_ERR_INVALID_ARG;
+  if (N >= kMaxDim || K >= kMaxDim) return I8MM_ERR_UNSUPPORTED;
+  if (N == 0) return I8MM_OK;
+  if (!SCB || !aligned(SCB, 4)) return I8MM_ERR_INVALID_ARG;
+  if (K > 0 && (!W || !CB || !aligned(W, 2))) return I8MM_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  const bool vec = (K % 8 == 0) && aligned(W, 16) && aligned(CB, 8);
+  launch_wquant((const _Float16*)W, N, K, CB, SCB, vec, stream);
+  return hip_status();
+}
+
+i8mm_status int8_linear_workspace_layout(int64_t T, int64_t N, int64_t K, int64_t max_outliers,
+                                         i8mm_ws_layout* out) {
+  if (!out) return I8MM_ERR_INVALID_ARG;
+  return layout_of(T, N, K, max_outliers, out);
+}
+
+size_t int8_linear_workspace_size(int64_t T, int64_t N, int64_t K, int64_t max_outliers) {
+  i8mm_ws_layout L;
+  if (layout_of(T, N, K, max_outliers, &L) != I8MM_OK) return 0;
+  return L.total;
+}
+
+i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_t* CB,
+                                const float* SCB, int64_t N, const void* bias, float threshold,
+                                void* Y, void* ws, size_t ws_bytes, int64_t max_outliers,
+                                hipStream_t stream) {
+  if (isnan(threshold) || !(threshold > 0.0f)) return I8MM_ERR_INVALID_ARG;
+  i8mm_ws_layout L;
+  const i8mm_status ls = layout_of(T, N, K, max_outliers, &L);
+  if (ls != I8MM_OK) return ls;
+  if (T == 0 || N == 0) return I8MM_OK;
+  if (!Y || !ws || !aligned(Y, 2) || !aligned(ws, kAlign)) return I8MM_ERR_INVALID_ARG;
+  if (bias && !aligned(bias, 2)) return I8MM_ERR_INVALID_ARG;
+  if (K > 0 && (!X || !CB || !SCB || !aligned(X, 2) || !aligned(SCB, 4)))
+    return I8MM_ERR_INVALID_ARG;
+  if (ws_bytes < L.total) return I8MM_ERR_WORKSPACE;
+  (void)hipGetLastError();
+
+  char* w = (char*)ws;
+  int32_t* counts = (int32_t*)(w + L.counts);
+  if (K == 0) {
+    launch_fill_bias((_Float16*)Y, T, N, (const _Float16*)bias, counts, stream);
+    return hip_status();
+  }
+
+  hipEvent_t* ev = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_on && g_prof_n < kProfCap) ev = &g_prof_ev[(size_t)(g_prof_n++) * 4];
+  }
+  if (ev) (void)hipEventRecord(ev[0], stream);
+
+  int32_t* O = (int32_t*)(w + L.outliers);
+  uint32_t* mask = (uint32_t*)(w + L.mask);
+  const DetectGeom g = detect_geom(T, K);
+  const bool xvec = (K % 8 == 0) && aligned(X, 16);
+  launch_detect((const _Float16*)X, T, K, threshold, (uint32_t*)(w + L.partial),
+                g.rows_per_block, g.nrb, mask, O, counts, max_outliers, xvec, stream);
+  if (ev) (void)hipEventRecord(ev[1], stream);
+
+  int8_t* Xq = (int8_t*)(w + L.xq);
+  float* sx = (float*)(w + L.sx);
+  _Float16* Xo = (_Float16*)(w + L.xo);
+  _Float16* Wo = (_Float16*)(w + L.wo);
+  launch_rowquant((const _Float16*)X, T, K, O, counts, mask, max_outliers, Xq, L.ldq, sx, Xo,
+                  L.ldo, CB, SCB, N, Wo, xvec, stream);
+  if (ev) (void)hipEventRecord(ev[2], stream);
+
+  GemmArgs a{};
+  a.A = CB;
+  a.lda = K;
+  a.B = Xq;
+  a.ldb = L.ldq;
+  a.N = N;
+  a.T = T;
+  a.K = K;
+  a.sx = sx;
+  a.SCB = SCB;
+  a.Wo = Wo;
+  a.Xo = Xo;
+  a.ldo = L.ldo;
+  a.counts = counts;
+  a.max_o = max_outliers;
+  a.bias = (const _Float16*)bias;
+  a.Y = (_Float16*)Y;
+  if (launch_gemm_fused(a, stream) != hipSuccess) return I8MM_ERR_HIP;
+  if (ev) (void)hipEventRecord(ev[3], stream);
+  return hip_status();
+}
+
+i8mm_status int8_linear_status(const void* ws, int32_t* n_outliers, hipStream_t stream) {
+  if (!ws || !aligned(ws, kAlign)) return I8MM_ERR_INVALID_ARG;
+  int32_t c[4] = {0, 0, 0, 0};
+  if (hipMemcpyAsync(c, ws, sizeof(c), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return I8MM_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return I8MM_ERR_HIP;
+  if (n_outliers) *n_outliers = c[0];
+  return c[1] ? I8MM_ERR_OUTLIER_OVERFLOW : I8MM_OK;
+}
+
+size_t int8_find_outliers_scratch_size(int64_t T, int64_t K) {
+  if (T < 0 || K < 0) return 0;
+  const DetectGeom g = detect_geom(T, K);
+  return (size_t)(g.nrb * (ceil_div(K, 32) > 0 ? ceil_div(K, 32) : 1)) * 4;
+}
+
+i8mm_status int8_find_outliers(const void* X, int64_t T, int64_t K, float threshold, int32_t* O,
+                               int32_t* counts, uint32_t* mask, int64_t max_outliers,
+                               void* partial, size_t partial_bytes, hipStream_t stream) {
+  if (isnan(threshold) || !(threshold > 0.0f)) return I8MM_ERR_INVALID_ARG;
+  if (T <= 0 || K <= 0 || max_outliers < 0 || max_outliers > K) return I8MM_ERR_INVALID_ARG;
+  if (T >= kMaxDim || K > kMaxK) return I8MM_ERR_UNSUPPORTED;
+  if (!X || !O || !counts || !mask || !partial || !aligned(X, 2) || !aligned(O, 4) ||
+      !aligned(counts, 4) || !aligned(mask, 4) || !aligned(partial, 4))
+    return I8MM_ERR_INVALID_ARG;
+  if (partial_bytes < int8_find_outliers_scratch_size(T, K)) return I8MM_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  const DetectGeom g = detect_geom(T, K);
+  const bool xvec = (K % 8 == 0) && aligned(X, 16);
+  launch_detect((const _Float16*)X, T, K, threshold, (uint32_t*)partial, g.rows_per_block, g.nrb,
+                mask, O, counts, max_outliers, xvec, stream);
+  return hip_status();
+}
+
+i8mm_status int8_quantize_rows(const void* X, int64_t T, int64_t K, const int32_t* O,
+                               const int32_t* counts, const uint32_t* mask, int64_t max_outliers,
+                               int8_t* Xq, int64_t ldq, float* sx, void* Xo, int64_t ldo,
+                               hipStream_t stream) {
+  if (T <= 0 || K <= 0 || max_outliers < 0 || max_outliers > K) return I8MM_ERR_INVALID_ARG;
+  if (T >= kMaxDim || K > kMaxK) return I8MM_ERR_UNSUPPORTED;
+  if (ldq < K || ldq % 16 != 0 || ldo < round_up(max_outliers, 32) || ldo % 32 != 0)
+    return I8MM_ERR_INVALID_ARG;
+  if (!X || !O || !counts || !Xq || !sx || !Xo || !aligned(X, 2) || !aligned(Xq, 16) ||
+      !aligned(sx, 4) || !aligned(Xo, 2) || (mask && !aligned(mask, 4)))
+    return I8MM_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  const bool xvec = (K % 8 == 0) && aligned(X, 16);
+  launch_rowquant((const _Float16*)X, T, K, O, counts, mask, max_outliers, Xq, ldq, sx,
+                  (_Float16*)Xo, ldo, nullptr, nullptr, 0, nullptr, xvec, stream);
+  return hip_status();
+}
+
+i8mm_status int8_outlier_weights(const int8_t* CB, const float* SCB, int64_t N, int64_t K,
+                                 const int32_t* O, const int32_t* counts, int64_t max_outliers,
+                                 void* Wo, int64_t ldo, hipStream_t stream) {
+  if (N <= 0 || K <= 0 || max_outliers < 0 || max_outliers > K) return I8MM_ERR_INVALID_ARG;
+  if (N >= kMaxDim || K > kMaxK) return I8MM_ERR_UNSUPPORTED;
+  if (ldo < round_up(max_outliers, 32) || ldo % 32 != 0) return I8MM_ERR_INVALID_ARG;
+  if (!CB || !SCB || !O || !counts || !Wo || !aligned(SCB, 4) || !aligned(Wo, 2))
+    return I8MM_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  launch_rowquant(nullptr, 0, K, O, counts, nullptr, max_outliers, nullptr, 0, nullptr, nullptr,
+                  ldo, CB, SCB, N, (_Float16*)Wo, false, stream);
+  return hip_status();
+}
+
+i8mm_status int8_gemm_s32(const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb, int32_t* C,
+                          int64_t T, int64_t N, int64_t K, hipStream_t stream) {
+  if (T < 0 || N < 0 || K < 0 || lda < K || ldb < K) return I8MM_ERR_INVALID_ARG;
+  if (T >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return I8MM_ERR_UNSUPPORTED;
+  if (T == 0 || N == 0) return I8MM_OK;
+  if (!C || !aligned(C, 4) || (K > 0 && (!A || !B))) return I8MM_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  GemmArgs a{};
+  a.A = B;  // weight side (rows = output columns of C)
+  a.lda = ldb;
+  a.B = A;  // activation side (rows = rows of C)
+  a.ldb = lda;
+  a.N = N;
+  a.T = T;
+  a.K = K;
+  a.C = C;
+  if (launch_gemm_s32(a, stream) != hipSuccess) return I8MM_ERR_HIP;
+  return hip_status();
+}
+
+i8mm_status i8mm_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on && g_prof_ev.empty()) {
+    g_prof_ev.resize((size_t)kProfCap * 4);
+    for (auto& e : g_prof_ev)
+      if (hipEventCreate(&e) != hipSuccess) return I8MM_ERR_HIP;
+  }
+  g_prof_on = on != 0;
+  g_prof_n = 0;
+  return I8MM_OK;
+}
+
+i8mm_status i8mm_profile_read(double* ms_sum, int64_t* calls) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double acc[4] = {0, 0, 0, 0};
+  for (int c = 0; c < g_prof_n; ++c) {
+    hipEvent_t* ev = &g_prof_ev[(size_t)c * 4];
+    if (hipEventSynchronize(ev[3]) != hipSuccess) return I8MM_ERR_HIP;
+    float t;
+    for (int s = 0; s < 3; ++s) {
+      if (hipEventElapsedTime(&t, ev[s], ev[s + 1]) != hipSuccess) return I8MM_ERR_HIP;
+      acc[s] += t;
+    }
+    if (hipEventElapsedTime(&t, ev[0], ev[3]) != hipSuccess) return I8MM_ERR_HIP;
+    acc[3] += t;
+  }
+  for (int s = 0; s < 4; ++s) {
+    if (ms_sum) ms_sum[s] = acc[s];
+    if (calls) calls[s] = g_prof_n;
+  }
+  return I8MM_OK;
+}
+
+}  // extern "C"

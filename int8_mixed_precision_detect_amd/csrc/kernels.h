@@ -1,0 +1,44 @@
+// Internal launchers of libi8mm (host side).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8mm {
+
+void launch_wquant(const _Float16* W, int64_t N, int64_t K, int8_t* CB, float* SCB, bool vec,
+                   hipStream_t st);
+void launch_detect(const _Float16* X, int64_t T, int64_t K, float thr, uint32_t* partial,
+                   int64_t rows_per_block, int64_t nrb, uint32_t* mask, int32_t* O,
+                   int32_t* counts, int64_t max_o, bool vec, hipStream_t st);
+void launch_rowquant(const _Float16* X, int64_t T, int64_t K, const int32_t* O,
+                     const int32_t* counts, const uint32_t* mask, int64_t max_o, int8_t* Xq,
+                     int64_t ldq, float* sx, _Float16* Xo, int64_t ldo, const int8_t* CB,
+                     const float* SCB, int64_t N, _Float16* Wo, bool vec, hipStream_t st);
+void launch_fill_bias(_Float16* Y, int64_t T, int64_t N, const _Float16* bias, int32_t* counts,
+                      hipStream_t st);
+
+// Fused product: Y = fp16(acc*sx*SCB/127^2 + Xo.Wo^T + bias), acc = Xq.CB^T.
+struct GemmArgs {
+  const int8_t* A;  // CB [N][lda] (features)
+  int64_t lda;
+  const int8_t* B;  // Xq [T][ldb] (tokens)
+  int64_t ldb;
+  int64_t N, T, K;
+  // fused epilogue
+  const float* sx;
+  const float* SCB;
+  const _Float16* Wo;
+  const _Float16* Xo;
+  int64_t ldo;
+  const int32_t* counts;
+  int64_t max_o;
+  const _Float16* bias;
+  _Float16* Y;
+  // int32 output instead of the epilogue
+  int32_t* C;
+};
+hipError_t launch_gemm_fused(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_s32(const GemmArgs& a, hipStream_t st);
+
+}  // namespace i8mm

@@ -31,3 +31,29 @@ def read_golden(name):
 @pytest.fixture
 def golden():
     return read_golden
+
+
+def ensure_built():
+    """Build libi8mm.so only if it is not there (the GPU machine gets it prebuilt)."""
+    from int8_mixed_precision_detect_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from int8_mixed_precision_detect_amd import build
+        build.build()
+    return _lib.LIB_PATH
+
+
+def gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def pytest_collection_modifyitems(config, items):
+    if gpu_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU in this process")
+    for it in items:
+        if "gpu" in it.keywords:
+            it.add_marker(skip)

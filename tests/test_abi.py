@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+include/i8mm.h declares, and rejects bad arguments before touching a GPU."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT, ensure_built
+
+HEADER = os.path.join(ROOT, "include", "i8mm.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def L():
+    ensure_built()
+    from int8_mixed_precision_detect_amd._lib import lib
+    return lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("int8_quantize_weight", "int8_linear_forward", "int8_linear_workspace_size",
+                     "int8_linear_status", "int8_find_outliers", "int8_quantize_rows",
+                     "int8_outlier_weights", "int8_gemm_s32"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from int8_mixed_precision_detect_amd._lib import SIGNATURES
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(L, n), f"libi8mm.so does not export {n}"
+        assert n in SIGNATURES, f"binding has no signature for {n}"
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.i8mm_abi_version() == 1
+    for code, name in [(0, b"I8MM_OK"), (1, b"I8MM_ERR_INVALID_ARG"), (2, b"I8MM_ERR_WORKSPACE"),
+                       (3, b"I8MM_ERR_UNSUPPORTED"), (4, b"I8MM_ERR_HIP"),
+                       (5, b"I8MM_ERR_OUTLIER_OVERFLOW")]:
+        assert L.i8mm_status_string(code) == name
+
+
+def test_workspace_layout(L):
+    from int8_mixed_precision_detect_amd._lib import WsLayout
+    for T, N, K, mo in [(16, 64, 64, 64), (2048, 20480, 5120, 5120), (1, 49152, 12288, 12288),
+                        (7, 5, 3, 0), (0, 4, 8, 8)]:
+        lay = WsLayout()
+        assert L.int8_linear_workspace_layout(T, N, K, mo, ctypes.byref(lay)) == 0
+        regions = [("counts", 16), ("outliers", max(mo, 1) * 4),
+                   ("mask", max(math.ceil(K / 32), 1) * 4),
+                   ("partial", lay.n_row_blocks * max(math.ceil(K / 32), 1) * 4),
+                   ("sx", T * 4), ("xq", T * lay.ldq), ("xo", T * lay.ldo * 2),
+                   ("wo", N * lay.ldo * 2)]
+        end = 0
+        for name, size in regions:
+            off = getattr(lay, name)
+            assert off % 256 == 0, name
+            assert off >= end, name
+            end = off + size
+        assert lay.total >= end
+        assert lay.ldq % 64 == 0 and lay.ldq >= K
+        assert lay.ldo % 32 == 0 and lay.ldo >= mo
+        assert L.int8_linear_workspace_size(T, N, K, mo) == lay.total
+
+
+def test_invalid_arguments_are_rejected_on_the_host(L):
+    nan = float("nan")
+    fwd = L.int8_linear_forward
+    # threshold NaN / <= 0
+    for thr in (nan, 0.0, -1.0):
+        assert fwd(None, 4, 8, None, None, 4, None, thr, None, None, 0, 8, None) == 1
+    # negative sizes, max_outliers outside [0, K]
+    assert fwd(None, -1, 8, None, None, 4, None, 6.0, None, None, 0, 8, None) == 1
+    assert fwd(None, 4, 8, None, None, 4, None, 6.0, None, None, 0, 9, None) == 1
+    assert fwd(None, 4, 8, None, None, 4, None, 6.0, None, None, 0, -1, None) == 1
+    # empty problems are no-ops
+    assert fwd(None, 0, 8, None, None, 4, None, 6.0, None, None, 0, 8, None) == 0
+    assert fwd(None, 4, 8, None, None, 0, None, 6.0, None, None, 0, 8, None) == 0
+    # null outputs / workspace
+    assert fwd(1 << 20, 4, 8, 1 << 20, 1 << 20, 4, None, 6.0, None, None, 0, 8, None) == 1
+    # workspace too small (checked before any launch)
+    need = L.int8_linear_workspace_size(4, 4, 8, 8)
+    assert fwd(1 << 20, 4, 8, 1 << 20, 1 << 20, 4, None, 6.0, 1 << 20, 1 << 24, need - 1, 8,
+               None) == 2
+    # misaligned workspace
+    assert fwd(1 << 20, 4, 8, 1 << 20, 1 << 20, 4, None, 6.0, 1 << 20, (1 << 24) + 8, need, 8,
+               None) == 1
+    # too-large K for the LDS mask copy
+    assert L.int8_linear_workspace_size(4, 4, (1 << 18) + 1, 0) == 0
+    q = L.int8_quantize_weight
+    assert q(None, -1, 4, None, None, None) == 1
+    assert q(None, 0, 4, None, None, None) == 0
+    assert L.int8_gemm_s32(None, 3, None, 4, None, 2, 2, 4, None) == 1   # lda < K
+    assert L.int8_find_outliers(None, 4, 8, nan, None, None, None, 8, None, 0, None) == 1
+    assert L.int8_quantize_rows(1 << 20, 4, 8, 1 << 20, 1 << 20, None, 8, 1 << 20, 8,
+                                1 << 20, 1 << 20, 32, None) == 1  # ldq % 16 != 0
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    import int8_mixed_precision_detect_amd as i8
+    with pytest.raises(ValueError):
+        i8.quantize_weight(torch.zeros((4, 4), dtype=torch.float16))
+    with pytest.raises(TypeError):
+        i8.quantize_weight(torch.zeros((4, 4), dtype=torch.float32))

@@ -1,0 +1,198 @@
+"""End-to-end parity of int8_linear_forward with the CPU oracle.
+
+Y must be within 2e-3 * max|Y| + 1 fp16 ulp of the oracle per element; the
+intermediate results the forward leaves in its workspace (O, n_o, sx, Xq, Xo,
+Wo) must match the oracle bit for bit.  Small shapes are checked in full;
+the workloads at full size are checked on sampled rows and output channels
+(detection still runs over all of X on both sides).
+"""
+import numpy as np
+import pytest
+
+import oracle.llm_int8 as O
+from tests.gpu_util import assert_y_close, dev, host, say
+from workloads import WORKLOADS, make_inputs, make_random_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def i8():
+    from tests.conftest import ensure_built
+    ensure_built()
+    import int8_mixed_precision_detect_amd as m
+    return m
+
+
+def _run(i8, X, W, bias, thr, max_outliers=None):
+    import torch
+    T, K = X.shape
+    N = W.shape[0]
+    Xd, Wd = dev(X), dev(W)
+    CB, SCB = i8.quantize_weight(Wd)
+    bd = None if bias is None else dev(bias)
+    mo = K if max_outliers is None else max_outliers
+    ws = i8.alloc_workspace(T, N, K, mo)
+    Y = i8.linear_forward(Xd, CB, SCB, bd, thr, max_outliers=mo, workspace=ws)
+    torch.cuda.synchronize()
+    return Y, ws, CB, SCB
+
+
+def _ws_views(i8, ws, T, N, K, mo):
+    lay = i8.workspace_layout(T, N, K, mo)
+    b = host(ws)
+    cnt = b[lay["counts"]: lay["counts"] + 16].view(np.int32)
+    n = int(cnt[0])
+    nu = min(n, mo)
+    Og = b[lay["outliers"]: lay["outliers"] + 4 * nu].view(np.int32)
+    sx = b[lay["sx"]: lay["sx"] + 4 * T].view(np.float32)
+    ldq, ldo = lay["ldq"], lay["ldo"]
+    Xq = b[lay["xq"]: lay["xq"] + T * ldq].view(np.int8).reshape(T, ldq)
+    Xo = b[lay["xo"]: lay["xo"] + T * ldo * 2].view(np.float16).reshape(T, ldo)
+    Wo = b[lay["wo"]: lay["wo"] + N * ldo * 2].view(np.float16).reshape(N, ldo)
+    return dict(counts=cnt, O=Og, sx=sx, Xq=Xq, Xo=Xo, Wo=Wo)
+
+
+def _full_check(i8, X, W, bias, thr, what):
+    T, K = X.shape
+    N = W.shape[0]
+    say("forward", what, T, K, N, thr)
+    Y, ws, CB, SCB = _run(i8, X, W, bias, thr)
+    CBo, SCBo = O.quantize_weight(W)
+    Yo, st = O.linear_forward(X, CBo, SCBo, bias, thr, return_stages=True)
+    err = assert_y_close(host(Y), Yo, what)
+    v = _ws_views(i8, ws, T, N, K, K)
+    n = len(st["O"])
+    assert v["counts"][0] == n and v["counts"][1] == 0
+    assert np.array_equal(v["O"], st["O"].astype(np.int32))
+    assert np.array_equal(v["sx"].view(np.uint32), st["sx"].view(np.uint32))
+    assert np.array_equal(v["Xq"][:, :K], st["Xq"])
+    assert np.all(v["Xq"][:, K:] == 0)
+    assert np.array_equal(v["Xo"][:, :n].view(np.uint16), st["Xo"].view(np.uint16))
+    assert np.array_equal(v["Wo"][:, :n].view(np.uint16), st["Wo"].view(np.uint16))
+    npad = ((n + 31) // 32) * 32
+    assert np.all(v["Xo"][:, n:npad].view(np.uint16) == 0)
+    assert np.all(v["Wo"][:, n:npad].view(np.uint16) == 0)
+    code, nn = i8.linear_status(ws)
+    assert code == 0 and nn == n
+    return Y, Yo, err
+
+
+def test_tiny_workload(i8):
+    d = make_inputs("tiny")
+    _, _, err = _full_check(i8, d["X"], d["W"], d["bias"], d["threshold"], "tiny")
+    print("tiny max err", err)
+
+
+RAGGED = [  # (T, K, N, planted, bias)
+    (300, 1024, 517, 3, True), (257, 1000, 300, 2, False), (513, 2048, 777, 40, True),
+    (1, 64, 1, 1, True), (2, 8, 3, 0, False), (600, 520, 1030, 5, True), (64, 4160, 256, 33, True),
+    (33, 1, 5, 1, True),
+]
+
+
+@pytest.mark.parametrize("T,K,N,planted,bias", RAGGED)
+def test_ragged_shapes(i8, T, K, N, planted, bias):
+    d = make_random_case(T + 3 * K + 7 * N, T, K, N, n_planted=planted, row_frac=0.5, bias=bias)
+    _full_check(i8, d["X"], d["W"], d["bias"], 6.0, f"ragged {T}x{K}x{N}")
+
+
+def test_no_outliers_threshold_inf(i8):
+    d = make_random_case(901, 200, 512, 300, n_planted=4)
+    _, _, _ = _full_check(i8, d["X"], d["W"], d["bias"], float("inf"), "thr=inf")
+
+
+def test_every_column_outlier(i8):
+    d = make_random_case(902, 96, 256, 130)
+    assert np.all(d["X"] != 0)
+    _full_check(i8, d["X"], d["W"], d["bias"], 1e-6, "n_o=K")
+
+
+def test_zero_rows_and_threshold_tie(i8):
+    d = make_random_case(903, 70, 320, 90, n_planted=2)
+    X, W = d["X"].copy(), d["W"].copy()
+    X[3] = 0                       # all-zero activation row
+    W[5] = 0                       # all-zero weight row
+    X[10, 7] = 6.0                 # exactly the threshold: column 7 is an outlier
+    X[:, 8] = np.float16(5.99609375)  # just below it: column 8 is not
+    _full_check(i8, X, W, d["bias"], 6.0, "zero rows / tie")
+
+
+def test_k_zero_gives_bias(i8):
+    import torch
+    T, N = 5, 7
+    bias = np.arange(N, dtype=np.float16)
+    say("forward K=0")
+    X = torch.empty((T, 0), dtype=torch.float16, device="cuda")
+    CB = torch.empty((N, 0), dtype=torch.int8, device="cuda")
+    SCB = torch.zeros(N, dtype=torch.float32, device="cuda")
+    Y = i8.linear_forward(X, CB, SCB, dev(bias), 6.0)
+    assert np.array_equal(host(Y), np.broadcast_to(bias, (T, N)))
+    Y = i8.linear_forward(X, CB, SCB, None, 6.0)
+    assert np.all(host(Y) == 0)
+
+
+def test_outlier_overflow_is_reported(i8):
+    d = make_random_case(904, 64, 256, 64, n_planted=10)
+    say("forward overflow")
+    Y, ws, _, _ = _run(i8, d["X"], d["W"], d["bias"], 6.0, max_outliers=4)
+    code, n = i8.linear_status(ws)
+    assert code == 5 and n == 10
+
+
+def test_deterministic(i8):
+    d = make_random_case(905, 513, 2048, 700, n_planted=7)
+    say("forward determinism")
+    Y1, _, _, _ = _run(i8, d["X"], d["W"], d["bias"], 6.0)
+    Y2, _, _, _ = _run(i8, d["X"], d["W"], d["bias"], 6.0)
+    assert np.array_equal(host(Y1).view(np.uint16), host(Y2).view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled
+# ---------------------------------------------------------------------------
+
+def _sampled_check(i8, name, n_rows=48, n_cols=384, cache={}):
+    import torch
+    wl = WORKLOADS[name]
+    key = "decode" if name.startswith("decode") else name
+    if key not in cache:
+        cache.clear()
+        dW = make_inputs(name)
+        Wd = dev(dW["W"])
+        CB, SCB = i8.quantize_weight(Wd)
+        cache[key] = (dW["W"], CB, SCB)
+    W, CB, SCB = cache[key]
+    d = make_inputs(name, with_weight=False)
+    X, bias, thr = d["X"], d["bias"], d["threshold"]
+    T, K, N = wl.T, wl.K, wl.N
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(T, size=min(n_rows, T), replace=False))
+    cols = np.sort(rng.choice(N, size=min(n_cols, N), replace=False))
+    # CB/SCB on the sampled channels: bit-exact against the oracle
+    CBo, SCBo = O.quantize_weight(W[cols])
+    assert np.array_equal(host(CB[torch.from_numpy(cols).cuda()]), CBo)
+    assert np.array_equal(host(SCB[torch.from_numpy(cols).cuda()]).view(np.uint32),
+                          SCBo.view(np.uint32))
+    say("forward full-size", name, T, K, N)
+    ws = i8.alloc_workspace(T, N, K)
+    Y = i8.linear_forward(dev(X), CB, SCB, None if bias is None else dev(bias), thr, workspace=ws)
+    Ys = host(Y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+    Yo, Oo = O.linear_forward_sampled(X, CBo, SCBo, None if bias is None else bias[cols], thr, rows)
+    err = assert_y_close(Ys, Yo, name)
+    code, n = i8.linear_status(ws)
+    assert code == 0 and n == len(Oo)
+    v = _ws_views(i8, ws, T, N, K, K)
+    assert np.array_equal(v["O"], Oo.astype(np.int32))
+    Xqo, sxo = O.quantize_rows(X[rows], Oo)
+    assert np.array_equal(v["sx"][rows].view(np.uint32), sxo.view(np.uint32))
+    assert np.array_equal(v["Xq"][rows, :K], Xqo)
+    print(name, "n_o", n, "max err", err)
+    return n
+
+
+@pytest.mark.parametrize("name", ["6.7b", "13b", "175b", "decode1", "decode8", "decode32"])
+def test_full_size_workload_sampled(i8, name):
+    n = _sampled_check(i8, name)
+    if name != "175b":
+        assert n == WORKLOADS[name].n_planted
