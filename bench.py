@@ -60,7 +60,7 @@ def read_traffic(workload: str):
         return None
 
 
-def cpu_baseline(d, cols: int):
+def cpu_baseline(d, cols: int, reps: int):
     """The oracle as it stands, on all rows and the first `cols` output channels."""
     import numpy as np
     import oracle.llm_int8 as O
@@ -69,7 +69,7 @@ def cpu_baseline(d, cols: int):
     CB, SCB = O.quantize_weight(W[:cols])          # load-time step, not timed
     b = None if bias is None else bias[:cols]
     times = []
-    for _ in range(3):
+    for _ in range(reps):
         t0 = time.perf_counter()
         O.linear_forward(X, CB, SCB, b, thr)
         times.append(time.perf_counter() - t0)
@@ -84,8 +84,8 @@ def cpu_baseline(d, cols: int):
     return {"value": 2.0 * T * cols * K / t / 1e12, "unit": "TOPS",
             "cores": threads or cores, "host_cores": cores, "kind": "oracle",
             "sample": f"full forward of the CPU oracle (NumPy, float64 BLAS) on all {T} rows and "
-                      f"the first {cols} of {W.shape[0]} output channels, median of 3 runs "
-                      f"({t:.2f} s each)"}
+                      f"the first {cols} of {W.shape[0]} output channels, median of {reps} runs "
+                      f"({t:.2f} s each, {sum(times):.1f} s in all)"}
 
 
 def main() -> int:
@@ -97,7 +97,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=3,
                     help="rotate this many copies of X/CB/SCB/Y so the 256 MB last-level "
                          "cache cannot hold one step's inputs from the step before")
-    ap.add_argument("--cpu-cols", type=int, default=10240)
+    ap.add_argument("--cpu-cols", type=int, default=20480)
+    ap.add_argument("--cpu-reps", type=int, default=11)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -226,7 +227,7 @@ def main() -> int:
         result["copy_calibration_bytes"] = nbytes
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d, min(args.cpu_cols, N))
+        result["cpu_baseline"] = cpu_baseline(d, min(args.cpu_cols, N), max(1, args.cpu_reps))
 
     print(json.dumps(result), flush=True)
     return 0
