@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
-GEMM_SOURCES = ["int8_mixed_precision_detect_amd/csrc/k_gemm.hip",
+GEMM_SOURCES = ["int8_mixed_precision_detect_amd/csrc/k_gemm_i8.hip",
                 "int8_mixed_precision_detect_amd/csrc/common.h",
                 "int8_mixed_precision_detect_amd/csrc/kernels.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_13b_traffic.txt")

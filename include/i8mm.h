@@ -95,6 +95,7 @@ typedef struct {
   size_t xq;       /* int8[T][ldq]: quantized X, outlier and pad columns 0     */
   size_t xo;       /* fp16[T][ldo]: X[:, O], zero-padded to ldo                */
   size_t wo;       /* fp16[N][ldo]: fp16(CB[:, O] * SCB / 127), zero-padded    */
+  size_t p;        /* fp32[T][N] outlier product, only when max_outliers > 96  */
   int64_t ldq;     /* row pitch of xq in bytes (K rounded up to 64)            */
   int64_t ldo;     /* row pitch of xo and wo in elements (max_outliers up to 32) */
   int64_t n_row_blocks;

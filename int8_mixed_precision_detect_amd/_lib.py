@@ -24,7 +24,7 @@ c_float = ctypes.c_float
 class WsLayout(ctypes.Structure):
     _fields_ = [
         ("counts", c_size), ("outliers", c_size), ("mask", c_size), ("partial", c_size),
-        ("sx", c_size), ("xq", c_size), ("xo", c_size), ("wo", c_size),
+        ("sx", c_size), ("xq", c_size), ("xo", c_size), ("wo", c_size), ("p", c_size),
         ("ldq", c_i64), ("ldo", c_i64), ("n_row_blocks", c_i64), ("total", c_size),
     ]
 

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libi8mm.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "k_prep.hip", "k_gemm.hip"]
+SOURCES = ["api.hip", "k_prep.hip", "k_gemm.hip", "k_gemm_i8.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -59,7 +59,7 @@ def build(verbose: bool = False) -> str:
             if verbose and out.strip():
                 print(out)
     tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -56,6 +56,7 @@ i8mm_status layout_of(int64_t T, int64_t N, int64_t K, int64_t max_o, i8mm_ws_la
   L->xq = take((size_t)T * (size_t)L->ldq);
   L->xo = take((size_t)T * (size_t)L->ldo * 2);
   L->wo = take((size_t)N * (size_t)L->ldo * 2);
+  L->p = take(max_o > kSmallTail ? (size_t)T * (size_t)N * 4 : 0);
   L->total = off;
   return I8MM_OK;
 }
@@ -177,7 +178,10 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   a.max_o = max_outliers;
   a.bias = (const _Float16*)bias;
   a.Y = (_Float16*)Y;
-  if (launch_gemm_fused(a, stream) != hipSuccess) return I8MM_ERR_HIP;
+  a.P = (float*)(w + L.p);
+  const hipError_t ge = gemm_i8_supported(a) ? launch_gemm_i8_fused(a, stream)
+                                             : launch_gemm_fused(a, stream);
+  if (ge != hipSuccess) return I8MM_ERR_HIP;
   if (ev) (void)hipEventRecord(ev[3], stream);
   return hip_status();
 }
@@ -264,7 +268,9 @@ i8mm_status int8_gemm_s32(const int8_t* A, int64_t lda, const int8_t* B, int64_t
   a.T = T;
   a.K = K;
   a.C = C;
-  if (launch_gemm_s32(a, stream) != hipSuccess) return I8MM_ERR_HIP;
+  const hipError_t ge = gemm_i8_supported(a) ? launch_gemm_i8_s32(a, stream)
+                                             : launch_gemm_s32(a, stream);
+  if (ge != hipSuccess) return I8MM_ERR_HIP;
   return hip_status();
 }
 

@@ -12,18 +12,22 @@
 // values are four consecutive output channels of one token and the fp16
 // store is one 8-byte write per lane.
 //
+// This is the general kernel: any K, any leading dimension, any alignment
+// (byte-granular loads), any number of outlier columns.  16-byte aligned
+// operands take the pipelined kernel in k_gemm_i8.hip instead.
+//
 // Tiling: a workgroup owns a BM x BN (channels x tokens) output tile, split
 // among waves of WM x WN, and walks K in 64-byte slices staged through LDS
 // (two buffers, register staged).  LDS rows are 64 bytes (4 chunks of 16); chunk cc of row r is
-// stored at chunk cc ^ s(r), s(r) = ((r>>1)&3) ^ ((r>>3)&1), which keeps the
-// 16-byte reads of 16 consecutive rows on distinct banks.
+// stored at chunk cc ^ ((r>>1)&3), which keeps the 16-byte fragment reads
+// free of bank conflicts on gfx950 (measured with SQ_LDS_BANK_CONFLICT).
 #include "common.h"
 #include "kernels.h"
 
 namespace i8mm {
 
 __device__ __forceinline__ int lds_off(int r, int cc) {
-  return r * 64 + ((cc ^ ((r >> 1) & 3) ^ ((r >> 3) & 1)) << 4);
+  return r * 64 + ((cc ^ ((r >> 1) & 3)) << 4);
 }
 
 // 16 bytes at byte offset k0 + kc of a row (p = row start); zero past Kb.
@@ -251,231 +255,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(GemmArgs a)
   }
 }
 
-// ---------------------------------------------------------------------------
-// Pipelined variant for 16-byte-aligned operands: the slices go global -> LDS
-// directly (global_load_lds_dwordx4), S slices in flight, one barrier per
-// slice.  A wave's load instruction writes 1 KB of LDS at consecutive lane
-// addresses, so the swizzle is applied on the global side: lane i of the
-// instruction covering rows 16j..16j+15 fetches logical chunk
-// (i%4) ^ s(row) of row 16j + i/4.  Chunks past the end of K read 16 zero
-// bytes from g_zero16 instead, so any K that is a multiple of 16 is exact.
-// ---------------------------------------------------------------------------
-__device__ __attribute__((aligned(16))) char g_zero16[16];
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // s_waitcnt with vmcnt = N and expcnt/lgkmcnt left at their maxima
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-template <int BM, int BN, int WM, int WN, int S, bool FUSED>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_dl(GemmArgs a) {
-  constexpr int NWN = BN / WN;
-  constexpr int NW = (BM / WM) * NWN;
-  constexpr int MI = WM / 16, NI = WN / 16;
-  constexpr int ACH = BM / 16, BCH = BN / 16;  // 1 KB pieces of a slice
-  constexpr int PW = (ACH + BCH) / NW;           // load instructions per wave per slice
-  static_assert((ACH + BCH) % NW == 0, "slice pieces must split evenly over the waves");
-  constexpr int STAGE = (BM + BN) * 64;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave / NWN) * WM, wn0 = (wave % NWN) * WN;
-
-  const int64_t tiles_m = ceil_div(a.N, BM), tiles_n = ceil_div(a.T, BN);
-  const int64_t ntiles = tiles_m * tiles_n;
-  int64_t bid = blockIdx.x;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-  const int64_t tn = bid % tiles_n, tm = bid / tiles_n;
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-
-  const char* gp[PW];
-  int lo_[PW], kc[PW];
-  auto setup = [&](const char* A, int64_t ldab, const char* B, int64_t ldbb) {
-#pragma unroll
-    for (int u = 0; u < PW; ++u) {
-      const int j = wave * PW + u;
-      const int rr = (j < ACH ? j : j - ACH) * 16 + (lane >> 2);
-      const int cc = (lane & 3) ^ ((rr >> 1) & 3) ^ ((rr >> 3) & 1);
-      if (j < ACH) {
-        const int64_t g = min(m0 + rr, a.N - 1);
-        gp[u] = A + g * ldab;
-        lo_[u] = j * 1024;
-      } else {
-        const int64_t g = min(n0 + rr, a.T - 1);
-        gp[u] = B + g * ldbb;
-        lo_[u] = BM * 64 + (j - ACH) * 1024;
-      }
-      kc[u] = cc * 16;
-    }
-  };
-  auto issue = [&](int buf, int64_t k0, int64_t Kb) {
-#pragma unroll
-    for (int u = 0; u < PW; ++u) {
-      const char* src = (k0 + kc[u] < Kb) ? gp[u] + k0 + kc[u] : g_zero16;
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (__attribute__((address_space(3))) void*)(lds + buf * STAGE + lo_[u]),
-                                       16, 0, 0);
-    }
-  };
-  const int lo = lds_off(lane & 15, lane >> 4);
-
-  v4i acc[MI][NI];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NI; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-  setup((const char*)a.A, a.lda, (const char*)a.B, a.ldb);
-  const int64_t nk = ceil_div(a.K, 64);
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue(s, s * 64, a.K);
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    if (nk - 1 - kt >= S - 2) wait_vmcnt<(S - 2) * PW>(); else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kt + S - 1 < nk) issue((int)((kt + S - 1) % S), (kt + S - 1) * 64, a.K);
-    const char* As = lds + (int)(kt % S) * STAGE;
-    const char* Bs = As + BM * 64;
-    v4i fa[MI], fb[NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i) fa[i] = *(const v4i*)(As + (wm0 + i * 16) * 64 + lo);
-#pragma unroll
-    for (int j = 0; j < NI; ++j) fb[j] = *(const v4i*)(Bs + (wn0 + j * 16) * 64 + lo);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
-  }
-
-  const int lrow = 4 * (lane >> 4);
-  const int lcol = lane & 15;
-  if constexpr (!FUSED) {
-    const bool cvec = ((a.N & 3) == 0) && ((((uintptr_t)a.C) & 15) == 0);
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int64_t f = m0 + wm0 + i * 16 + lrow;
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int64_t t = n0 + wn0 + j * 16 + lcol;
-        if (t >= a.T) continue;
-        int32_t* dst = a.C + t * a.N + f;
-        if (cvec && f + 3 < a.N) {
-          *(v4i*)dst = acc[i][j];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (f + r < a.N) dst[r] = acc[i][j][r];
-        }
-      }
-    }
-    return;
-  } else {
-    float sxv[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t t = n0 + wn0 + j * 16 + lcol;
-      sxv[j] = (t < a.T) ? a.sx[t] : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      float sc[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t f = m0 + wm0 + i * 16 + lrow + r;
-        sc[r] = (f < a.N) ? a.SCB[f] * (1.0f / 16129.0f) : 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        v4f v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (float)acc[i][j][r] * (sxv[j] * sc[r]);
-        acc[i][j] = __builtin_bit_cast(v4i, v);
-      }
-    }
-
-    const int64_t n_o = a.counts[0];
-    const int64_t n_use = n_o < a.max_o ? n_o : a.max_o;
-    const int64_t nt = ceil_div(n_use, 32);
-    if (nt > 0) {
-      const int64_t Kb = nt * 64;
-      __builtin_amdgcn_s_barrier();  // every wave is done reading the int8 slices
-      setup((const char*)a.Wo, a.ldo * 2, (const char*)a.Xo, a.ldo * 2);
-#pragma unroll
-      for (int s = 0; s < S - 1; ++s)
-        if (s < nt) issue(s, s * 64, Kb);
-      for (int64_t kt = 0; kt < nt; ++kt) {
-        if (nt - 1 - kt >= S - 2) wait_vmcnt<(S - 2) * PW>(); else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (kt + S - 1 < nt) issue((int)((kt + S - 1) % S), (kt + S - 1) * 64, Kb);
-        const char* As = lds + (int)(kt % S) * STAGE;
-        const char* Bs = As + BM * 64;
-        v8h fa[MI], fb[NI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) fa[i] = *(const v8h*)(As + (wm0 + i * 16) * 64 + lo);
-#pragma unroll
-        for (int j = 0; j < NI; ++j) fb[j] = *(const v8h*)(Bs + (wn0 + j * 16) * 64 + lo);
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < NI; ++j)
-            acc[i][j] = __builtin_bit_cast(
-                v4i, __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[j],
-                                                            __builtin_bit_cast(v4f, acc[i][j]), 0, 0, 0));
-      }
-    }
-
-    const bool yvec = ((a.N & 3) == 0) && ((((uintptr_t)a.Y) & 7) == 0);
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int64_t f = m0 + wm0 + i * 16 + lrow;
-      float bv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bv[r] = (a.bias && f + r < a.N) ? h2f(a.bias[f + r]) : 0.0f;
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int64_t t = n0 + wn0 + j * 16 + lcol;
-        if (t >= a.T) continue;
-        _Float16* dst = a.Y + t * a.N + f;
-        const v4f v = __builtin_bit_cast(v4f, acc[i][j]);
-        v4h y;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = (_Float16)(v[r] + bv[r]);
-        if (yvec && f + 3 < a.N) {
-          *(v4h*)dst = y;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (f + r < a.N) dst[r] = y[r];
-        }
-      }
-    }
-  }
-}
-
 template <int BM, int BN, int WM, int WN, bool FUSED>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   const int64_t ntiles = ceil_div(a.N, BM) * ceil_div(a.T, BN);
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
+  constexpr size_t LDS = 2 * (size_t)(BM + BN) * 64;
   const bool vec = (a.K % 16 == 0) && (a.lda % 16 == 0) && (a.ldb % 16 == 0) &&
                    ((((uintptr_t)a.A) & 15) == 0) && ((((uintptr_t)a.B) & 15) == 0);
+  hipError_t e;
   if (vec) {
-    // 16-byte aligned operands: the pipelined direct-to-LDS kernel
-    constexpr int S = 3;
-    constexpr size_t LDS = (size_t)S * (BM + BN) * 64;
-    auto kern = k_gemm_dl<BM, BN, WM, WN, S, FUSED>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
+    auto kern = k_gemm<BM, BN, WM, WN, FUSED, true>;
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
     if (e != hipSuccess) return e;
     kern<<<dim3((unsigned)ntiles), dim3(NT), LDS, st>>>(a);
   } else {
-    // any other K or leading dimension: byte-granular, register-staged loads
-    constexpr size_t LDS = 2 * (size_t)(BM + BN) * 64;
     auto kern = k_gemm<BM, BN, WM, WN, FUSED, false>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
     if (e != hipSuccess) return e;
     kern<<<dim3((unsigned)ntiles), dim3(NT), LDS, st>>>(a);
   }
@@ -483,7 +278,8 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
 }
 
 // 256 x 256 tile, 8 waves of 128 x 64 (two waves per SIMD): the fused
-// epilogue fits the register file without spilling at this wave tile.
+// epilogue, with its in-register fp16 loop over any number of outlier
+// columns, fits the register file without spilling at this wave tile.
 hipError_t launch_gemm_fused(const GemmArgs& a, hipStream_t st) {
   return launch_cfg<256, 256, 128, 64, true>(a, st);
 }

@@ -37,8 +37,24 @@ struct GemmArgs {
   _Float16* Y;
   // int32 output instead of the epilogue
   int32_t* C;
+  // fp32 [T][N] product over a large outlier set (more than kSmallTail
+  // columns); only read or written in that case
+  float* P;
 };
+
+// Outlier columns the aligned fused kernel handles inside its epilogue
+// (3 slices of 32, staged in LDS); beyond that a separate fp16 launch writes
+// P first.
+constexpr int64_t kSmallTail = 96;
+
+// Any shape and alignment: register-staged, byte-granular loads.
 hipError_t launch_gemm_fused(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_s32(const GemmArgs& a, hipStream_t st);
+
+// 16-byte aligned operands (K, lda, ldb multiples of 16): the pipelined
+// gfx950 kernel.
+bool gemm_i8_supported(const GemmArgs& a);
+hipError_t launch_gemm_i8_fused(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_i8_s32(const GemmArgs& a, hipStream_t st);
 
 }  // namespace i8mm

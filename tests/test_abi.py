@@ -62,7 +62,7 @@ def test_workspace_layout(L):
                    ("mask", max(math.ceil(K / 32), 1) * 4),
                    ("partial", lay.n_row_blocks * max(math.ceil(K / 32), 1) * 4),
                    ("sx", T * 4), ("xq", T * lay.ldq), ("xo", T * lay.ldo * 2),
-                   ("wo", N * lay.ldo * 2)]
+                   ("wo", N * lay.ldo * 2), ("p", T * N * 4 if mo > 96 else 0)]
         end = 0
         for name, size in regions:
             off = getattr(lay, name)
