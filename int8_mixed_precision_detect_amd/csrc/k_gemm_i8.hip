@@ -11,23 +11,28 @@
 //                                   set is too large for the fused epilogue
 //                                   (more than kSmallTail columns)
 //
-// Workgroup: 4 waves (one per SIMD), 256 x 256 output tile (channels x
-// tokens), 128 x 128 per wave = 8 x 8 blocks of v_mfma_i32_16x16x64_i8.  K is
-// walked in 64-byte slices; S slices are in flight in LDS, loaded with
-// buffer_load_dwordx4 ... lds (no staging registers), so a slice is
-// requested S slices ahead of its use.  Operand fragments are double-buffered in
-// registers: while the 64 MFMAs of slice k issue, the 16 LDS reads of slice
-// k+1 are interleaved between them.  One barrier per slice.
+// Workgroup: a BM x BN output tile (channels x tokens) split over waves of
+// WM x WN, each an array of 16 x 16 v_mfma_i32_16x16x64_i8 blocks.  K is
+// walked in slices of KB bytes per row (KB/64 MFMA k-steps each); S slices
+// are in flight in LDS, loaded with buffer_load_dwordx4 ... lds (no staging
+// registers), one barrier per slice.
 //
-// LDS rows are 64 bytes (4 chunks of 16); chunk cc of row r sits at chunk
-// cc ^ ((r>>1)&3).  Measured on gfx950 with the SQ_LDS_BANK_CONFLICT counter,
-// this makes the fragment reads (16 consecutive rows x 4 chunks per wave)
-// conflict-free at every row offset the kernel uses, ~4 LDS cycles per
-// 16-byte-per-lane read; an XOR that also folds in bit 3 of the row costs
-// twice that.  A load instruction writes 1 KB of LDS
-// at consecutive lane addresses, so the swizzle is applied on the global side
-// (lane i fetches the chunk that belongs at its LDS position).  Chunks past
-// the end of K read as zeros, so any K that is a multiple of 16 is exact.
+// Load efficiency: a load instruction fills 1 KB of LDS, i.e. 1024/KB rows
+// of KB bytes.  With KB = 128 every instruction reads whole 128-byte lines;
+// with 64-byte rows each instruction touches twice the lines for the same
+// bytes, and the memory pipeline alone of that variant took ~190 us of a
+// 261 us 13B-scale product.
+//
+// LDS rows are KB bytes (KB/16 chunks of 16); chunk c of row r sits at
+// chunk c ^ sw(r), sw(r) = (r>>1)&3 for 64-byte rows, r&7 for 128-byte rows.
+// Measured on gfx950 with the SQ_LDS_BANK_CONFLICT counter, both keep the
+// fragment reads (16 consecutive rows x 4 chunks per wave) conflict-free at
+// every row offset used here (~4 LDS cycles per 16-byte-per-lane read; an
+// XOR that also folds in row bit 3 on 64-byte rows costs twice that).  A
+// load instruction writes consecutive lane addresses, so the swizzle is
+// applied on the global side: lane i fetches the chunk that belongs at its
+// LDS position.  Chunks past the end of K read as zeros (their offset points
+// past the buffer's range), so any K that is a multiple of 16 is exact.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,8 +42,9 @@ namespace {
 
 constexpr int MODE_I32 = 0, MODE_FUSED = 1, MODE_F16 = 2;
 
-__device__ __forceinline__ int swz_off(int r, int cc) {
-  return r * 64 + ((cc ^ ((r >> 1) & 3)) << 4);
+template <int KB>
+__device__ __forceinline__ int swz(int r) {
+  return KB == 64 ? ((r >> 1) & 3) : (r & 7);
 }
 
 template <int N>
@@ -46,29 +52,46 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// wait until at most n*PW of this wave's loads are outstanding (n < 4)
+template <int PW>
+__device__ __forceinline__ void wait_slices(int n) {
+  if (n >= 3)
+    wait_vm<3 * PW < 64 ? 3 * PW : 63>();
+  else if (n == 2)
+    wait_vm<2 * PW>();
+  else if (n == 1)
+    wait_vm<PW>();
+  else
+    wait_vm<0>();
+}
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
 }  // namespace
 
-template <int BM, int BN, int WM, int WN, int S, bool DBUF, int MODE>
+template <int BM, int BN, int WM, int WN, int S, int KB, int MODE>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs a) {
   // The body uses amdgcn-only types (buffer resources); the host pass only
   // needs the kernel's signature to emit its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int MI = WM / 16, NI = WN / 16;
   constexpr int NWN = BN / WN, NWAVE = (BM / WM) * NWN;
-  constexpr int STAGE = (BM + BN) * 64;            // bytes of one slice
-  constexpr int PW = (BM / 16 + BN / 16) / NWAVE;  // 1 KB load instructions per wave per slice
-  static_assert((BM / 16 + BN / 16) % NWAVE == 0, "slice pieces must split evenly over waves");
-  static_assert((BM / 16) % PW == 0, "each wave loads pieces of one operand only");
+  constexpr int STAGE = (BM + BN) * KB;          // bytes of one slice
+  constexpr int RPP = 1024 / KB;                 // rows per 1 KB load instruction
+  constexpr int CPR = KB / 16;                   // 16-byte chunks per row
+  constexpr int ACH = BM / RPP, BCH = BN / RPP;  // load instructions per slice
+  constexpr int PW = (ACH + BCH) / NWAVE;        // ... per wave
+  constexpr int KS = KB / 64;                    // MFMA k-steps per slice
+  static_assert(KB == 64 || KB == 128, "slice width");
+  static_assert(S >= 2 && S <= 4 && (S - 1) * PW < 64, "slices in flight");
+  static_assert((ACH + BCH) % NWAVE == 0, "slice pieces must split evenly over waves");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / NWN) * WM, wn0 = (wave % NWN) * WN;
 
   // the outlier-product launch only has work for a large outlier set
-  int64_t nt_tail = 0;
+  int64_t nt_tail = 0;  // 32-column (64-byte) k-steps of the outlier operands
   if constexpr (MODE != MODE_I32) {
     const int64_t n_o = a.counts[0];
     const int64_t n_use = n_o < a.max_o ? n_o : a.max_o;
@@ -90,49 +113,53 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   // Slice loads: buffer_load_dwordx4 ... lds.  The operand is a buffer
   // resource (base in SGPRs), a lane's 32-bit offset (row * ld + its chunk)
   // is fixed for the whole K loop and the K position goes in the scalar
-  // offset, so a load costs no per-lane address arithmetic.  A chunk past the
-  // end of K gets an offset beyond the buffer's range, which the hardware
-  // reads as zeros.
+  // offset, so a load costs no per-lane address arithmetic.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff[PW], vtail[PW];
+  __amdgpu_buffer_rsrc_t rsA, rsB;
+  uint32_t voff[PW];
   int kc[PW];
   auto setup = [&](const char* A, int64_t ldab, int64_t rowsA, const char* B, int64_t ldbb,
                    int64_t rowsB) {
-    const bool isA = wv * PW < BM / 16;  // a wave's pieces are all A or all B
-    const char* base = isA ? A : B;
-    const int64_t ld = isA ? ldab : ldbb;
-    const int64_t rows = isA ? rowsA : rowsB;
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(rows * ld), 0x00020000);
+    rsA = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(rowsA * ldab), 0x00020000);
+    rsB = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(rowsB * ldbb), 0x00020000);
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
-      const int j = wv * PW + u;  // 1 KB piece: 16 rows of A, then of B
-      const int rr = (isA ? j : j - BM / 16) * 16 + (lane >> 2);
-      const int cc = (lane & 3) ^ ((rr >> 1) & 3);
+      const int j = wv * PW + u;  // piece: RPP rows of A, then of B (wave-uniform)
+      const bool isA = j < ACH;
+      const int rr = (isA ? j : j - ACH) * RPP + lane / CPR;
+      const int c = (lane % CPR) ^ swz<KB>(rr);
       const int64_t g = isA ? min(m0 + rr, a.N - 1) : min(n0 + rr, a.T - 1);
-      voff[u] = (uint32_t)(g * ld + cc * 16);
-      kc[u] = cc * 16;
+      voff[u] = (uint32_t)(g * (isA ? ldab : ldbb) + c * 16);
+      kc[u] = c * 16;
     }
   };
   auto lds_dst = [&](int buf, int u) {
     const int j = wv * PW + u;
-    const int off = (j < BM / 16) ? j * 1024 : BM * 64 + (j - BM / 16) * 1024;
+    const int off = (j < ACH) ? j * 1024 : BM * KB + (j - ACH) * 1024;
     return (__attribute__((address_space(3))) void*)(lds + buf * STAGE + off);
   };
   auto issue = [&](int buf, int64_t k0, int64_t Kb) {
-    if (k0 + 64 <= Kb) {
+    if (k0 + KB <= Kb) {
 #pragma unroll
       for (int u = 0; u < PW; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_dst(buf, u), 16, voff[u], (int)k0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wv * PW + u < ACH ? rsA : rsB, lds_dst(buf, u), 16,
+                                                 voff[u], (int)k0, 0, 0);
     } else {
 #pragma unroll
       for (int u = 0; u < PW; ++u) {
         const uint32_t vo = (k0 + kc[u] < Kb) ? voff[u] : 0x80000000u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_dst(buf, u), 16, vo, (int)k0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wv * PW + u < ACH ? rsA : rsB, lds_dst(buf, u), 16,
+                                                 vo, (int)k0, 0, 0);
       }
     }
   };
-  const int lo = swz_off(lane & 15, lane >> 4);
+  // fragment of 16 rows at k-step h of a slice: lane -> row (lane & 15),
+  // chunk (lane >> 4) + 4h
+  const int lr = lane & 15;
+  auto frag_off = [&](int row0, int h) {
+    const int r = row0 + lr;
+    return r * KB + ((((lane >> 4) + 4 * h) ^ swz<KB>(r)) << 4);
+  };
 
   v4i acc[MI][NI];
 #pragma unroll
@@ -150,107 +177,50 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, y, acc[i][j], 0, 0, 0);
     }
   };
-  auto read_frags = [&](int buf, v4i (&fa)[MI], v4i (&fb)[NI]) {
+  // the MFMAs of one slice; the other waves of the SIMD cover LDS latency
+  auto compute = [&](int buf) {
     const char* As = lds + buf * STAGE;
-    const char* Bs = As + BM * 64;
+    const char* Bs = As + BM * KB;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fa[i] = *(const v4i*)(As + (wm0 + i * 16) * 64 + lo);
+    for (int h = 0; h < KS; ++h) {
+      v4i fa[MI], fb[NI];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) fb[j] = *(const v4i*)(Bs + (wn0 + j * 16) * 64 + lo);
-  };
-  // 64 MFMAs on (ca, cb); one LDS read of the next slice after every 4th
-  auto step = [&](const v4i (&ca)[MI], const v4i (&cb)[NI], v4i (&na)[MI], v4i (&nb)[NI],
-                  int nbuf) {
-    const char* As = lds + nbuf * STAGE;
-    const char* Bs = As + BM * 64;
+      for (int i = 0; i < MI; ++i) fa[i] = *(const v4i*)(As + frag_off(wm0 + i * 16, h));
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+      for (int j = 0; j < NI; ++j) fb[j] = *(const v4i*)(Bs + frag_off(wn0 + j * 16, h));
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        mfma(i, j, ca[i], cb[j]);
-        if ((j & 3) == 3) {
-          const int f = (i * NI + j) >> 2;
-          if (f < MI)
-            na[f] = *(const v4i*)(As + (wm0 + f * 16) * 64 + lo);
-          else
-            nb[f - MI] = *(const v4i*)(Bs + (wn0 + (f - MI) * 16) * 64 + lo);
-        }
-      }
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) mfma(i, j, fa[i], fb[j]);
     }
   };
-  auto last = [&](const v4i (&ca)[MI], const v4i (&cb)[NI]) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j) mfma(i, j, ca[i], cb[j]);
-  };
 
-  int64_t nk, Kb;
+  int64_t Kb;
   if constexpr (MODE == MODE_F16) {
     setup((const char*)a.Wo, a.ldo * 2, a.N, (const char*)a.Xo, a.ldo * 2, a.T);
-    nk = nt_tail;
     Kb = nt_tail * 64;
   } else {
     setup((const char*)a.A, a.lda, a.N, (const char*)a.B, a.ldb, a.T);
-    nk = ceil_div(a.K, 64);
     Kb = a.K;
   }
-  // make slice kt+1 visible to every wave and start loading slice kt+S into
-  // the buffer slice kt used (its fragments are already in registers)
-  auto sync_next = [&](int64_t kt) {
-    wait_lgkm0();
-    if (kt + S - 1 <= nk - 1)
-      wait_vm<(S - 2) * PW>();
-    else
-      wait_vm<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kt + S < nk) issue((int)(kt % S), (kt + S) * 64, Kb);
-  };
+  const int64_t nk = ceil_div(Kb, KB);
 
   if (nk > 0) {
 #pragma unroll
     for (int s = 0; s < S; ++s)
-      if (s < nk) issue(s, s * 64, Kb);
-    if (nk >= S)
-      wait_vm<(S - 1) * PW>();
-    else
-      wait_vm<0>();
-    __builtin_amdgcn_s_barrier();
-    if constexpr (DBUF) {
-      // fragments double-buffered in registers: the reads of slice k+1
-      // interleave with the MFMAs of slice k
-      v4i fa0[MI], fb0[NI], fa1[MI], fb1[NI];
-      read_frags(0, fa0, fb0);
-      int64_t kt = 0;
-      for (; kt + 2 < nk; kt += 2) {
-        sync_next(kt);
-        step(fa0, fb0, fa1, fb1, (int)((kt + 1) % S));
-        sync_next(kt + 1);
-        step(fa1, fb1, fa0, fb0, (int)((kt + 2) % S));
-      }
-      if (nk - kt == 2) {
-        sync_next(kt);
-        step(fa0, fb0, fa1, fb1, (int)((kt + 1) % S));
-        last(fa1, fb1);
-      } else {
-        last(fa0, fb0);
-      }
-    } else {
-      // one fragment set; the other waves of the SIMD cover the LDS latency
-      for (int64_t kt = 0; kt < nk; ++kt) {
-        if (kt > 0) {
-          // slice kt must have landed; the buffer of slice kt-1 is free
-          if (kt + S - 2 <= nk - 1)
-            wait_vm<(S - 2) * PW>();
-          else
-            wait_vm<0>();
-          __builtin_amdgcn_s_barrier();
-          if (kt - 1 + S < nk) issue((int)((kt - 1) % S), (kt - 1 + S) * 64, Kb);
-        }
-        v4i fa[MI], fb[NI];
-        read_frags((int)(kt % S), fa, fb);
-        last(fa, fb);
-      }
+      if (s < nk) issue(s, s * KB, Kb);
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      // Slice kt must have landed.  Issued so far: slices up to
+      // min(kt + S - 2, nk - 1) (up to S - 1 before the loop); the ones
+      // after kt may stay in flight.
+      const int64_t last = kt == 0 ? (S - 1 < nk - 1 ? S - 1 : nk - 1)
+                                   : (kt + S - 2 < nk - 1 ? kt + S - 2 : nk - 1);
+      wait_slices<PW>((int)(last - kt));
+      // one barrier: slice kt is visible to every wave, and every wave is
+      // done with slice kt-1, whose buffer is refilled with slice kt-1+S
+      __builtin_amdgcn_s_barrier();
+      if (kt >= 1 && kt - 1 + S < nk) issue((int)((kt - 1) % S), (kt - 1 + S) * KB, Kb);
+      compute((int)(kt % S));
     }
   }
 
@@ -298,17 +268,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     }
   } else {
     // ---- fused epilogue ----
-    // small outlier sets: stage Xo/Wo (<= S slices of 32 columns) in LDS and
-    // run the fp16 MFMAs per output block into a fresh accumulator; large
-    // ones: the fp32 product P was written by the MODE_F16 launch before.
+    // small outlier sets: stage Xo/Wo (<= kSmallTail columns) in LDS and run
+    // the fp16 MFMAs per output block into a fresh accumulator; large ones:
+    // the fp32 product P was written by the MODE_F16 launch before.
     const bool small = nt_tail <= kSmallTail / 32;
+    const int64_t Kt = nt_tail * 64;        // bytes of a tail row
+    const int ntl = (int)ceil_div(Kt, KB);  // tail slices
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();  // every wave is done with the int8 slices
     if (small && nt_tail > 0) {
+      static_assert(S * KB >= kSmallTail * 2, "the small tail must fit the slice buffers");
       setup((const char*)a.Wo, a.ldo * 2, a.N, (const char*)a.Xo, a.ldo * 2, a.T);
-      static_assert(S * 32 >= kSmallTail, "the small tail must fit the slice buffers");
       for (int s = 0; s < S; ++s)
-        if (s < nt_tail) issue(s, s * 64, nt_tail * 64);
+        if (s < ntl) issue(s, s * KB, Kt);
       wait_vm<0>();
       __builtin_amdgcn_s_barrier();
     }
@@ -333,13 +305,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     v8h ta[MI];
     if (small && nt_tail == 1) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i) ta[i] = *(const v8h*)(lds + (wm0 + i * 16) * 64 + lo);
+      for (int i = 0; i < MI; ++i) ta[i] = *(const v8h*)(lds + frag_off(wm0 + i * 16, 0));
     }
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int64_t t = n0 + wn0 + j * 16 + lcol;
       v8h tb = {};
-      if (small && nt_tail == 1) tb = *(const v8h*)(lds + BM * 64 + (wn0 + j * 16) * 64 + lo);
+      if (small && nt_tail == 1) tb = *(const v8h*)(lds + BM * KB + frag_off(wn0 + j * 16, 0));
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int64_t f = m0 + wm0 + i * 16 + lrow;
@@ -348,10 +320,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
           if (nt_tail == 1) {
             p = __builtin_amdgcn_mfma_f32_16x16x32_f16(ta[i], tb, p, 0, 0, 0);
           } else {
-            for (int64_t s = 0; s < nt_tail; ++s) {
-              const char* base = lds + s * STAGE;
-              const v8h xa = *(const v8h*)(base + (wm0 + i * 16) * 64 + lo);
-              const v8h xb = *(const v8h*)(base + BM * 64 + (wn0 + j * 16) * 64 + lo);
+            for (int64_t q = 0; q < nt_tail; ++q) {  // 64-byte k-steps of the tail
+              const char* base = lds + (int)(q / KS) * STAGE;
+              const int h = (int)(q % KS);
+              const v8h xa = *(const v8h*)(base + frag_off(wm0 + i * 16, h));
+              const v8h xb = *(const v8h*)(base + BM * KB + frag_off(wn0 + j * 16, h));
               p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, xb, p, 0, 0, 0);
             }
           }
@@ -384,40 +357,41 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
 }
 
 #ifndef I8MM_CFG
-#define I8MM_CFG 3
+#define I8MM_CFG 20
 #endif
 
 namespace {
-template <int BM, int BN, int WM, int WN, int S, bool DBUF, int MODE>
+template <int BM, int BN, int WM, int WN, int S, int KB, int MODE>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  constexpr size_t LDS = (size_t)S * (BM + BN) * 64;
-  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_i8<BM, BN, WM, WN, S, DBUF, MODE>,
+  constexpr size_t LDS = (size_t)S * (BM + BN) * KB;
+  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_i8<BM, BN, WM, WN, S, KB, MODE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
   if (e != hipSuccess) return e;
   const int64_t ntiles = ceil_div(a.N, BM) * ceil_div(a.T, BN);
-  k_gemm_i8<BM, BN, WM, WN, S, DBUF, MODE><<<dim3((unsigned)ntiles), dim3(NT), LDS, st>>>(a);
+  k_gemm_i8<BM, BN, WM, WN, S, KB, MODE><<<dim3((unsigned)ntiles), dim3(NT), LDS, st>>>(a);
   return hipGetLastError();
 }
 
 // tile configurations: channels x tokens per workgroup, per wave, slices in
-// flight, register double-buffering of fragments.  Configuration 3 (256 x 256,
-// 8 waves of 64 x 128, 4 slices, single-buffered) measured fastest on the
-// first feed-forward shapes.
+// flight, slice bytes per row.  Configuration 20 (256 x 256, 8 waves of
+// 64 x 128, two 128-byte slices in flight, 128 KB of LDS) measured fastest
+// on the first feed-forward shapes (13B: 242 us against 275 us for the
+// 64-byte, four-slice configuration 3).
 template <int MODE>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
-#if I8MM_CFG == 0
-  return launch_cfg<256, 256, 128, 64, 4, false, MODE>(a, st);
-#elif I8MM_CFG == 1
-  return launch_cfg<256, 256, 128, 128, 4, true, MODE>(a, st);
-#elif I8MM_CFG == 3
-  return launch_cfg<256, 256, 64, 128, 4, false, MODE>(a, st);
-#elif I8MM_CFG == 4
-  return launch_cfg<256, 128, 128, 64, 3, false, MODE>(a, st);
-#elif I8MM_CFG == 5
-  return launch_cfg<256, 256, 128, 64, 3, false, MODE>(a, st);
-#elif I8MM_CFG == 6
-  return launch_cfg<128, 256, 64, 128, 3, false, MODE>(a, st);
+#if I8MM_CFG == 3
+  return launch_cfg<256, 256, 64, 128, 4, 64, MODE>(a, st);
+#elif I8MM_CFG == 20
+  return launch_cfg<256, 256, 64, 128, 2, 128, MODE>(a, st);
+#elif I8MM_CFG == 21
+  return launch_cfg<256, 128, 64, 64, 3, 128, MODE>(a, st);
+#elif I8MM_CFG == 22
+  return launch_cfg<256, 256, 128, 64, 2, 128, MODE>(a, st);
+#elif I8MM_CFG == 23
+  return launch_cfg<128, 256, 64, 64, 3, 128, MODE>(a, st);
+#elif I8MM_CFG == 24
+  return launch_cfg<256, 256, 64, 64, 2, 128, MODE>(a, st);
 #else
 #error "unknown I8MM_CFG"
 #endif
