@@ -157,6 +157,9 @@ i8mm_status int8_linear_status(const void* ws, int32_t* n_outliers, hipStream_t 
  * max_outliers), O[0 .. min(n_o, max_outliers)) ascending, and the bit mask
  * mask[ceil(K/32)] (bit k%32 of word k/32).  `partial` is scratch of
  * int8_find_outliers_scratch_size(T, K) bytes.  counts: int32[4].
+ * (The forward runs the same per-row-block detection kernel; its compaction
+ * happens inside the step-2 kernel, which publishes the same mask, O and
+ * counts into the workspace.)
  */
 size_t int8_find_outliers_scratch_size(int64_t T, int64_t K);
 i8mm_status int8_find_outliers(const void* X, int64_t T, int64_t K, float threshold,
@@ -165,26 +168,26 @@ i8mm_status int8_find_outliers(const void* X, int64_t T, int64_t K, float thresh
                                hipStream_t stream);
 
 /*
- * Step 2, activation side, for a given outlier set (O ascending, counts[0] =
- * n_o, only the first min(n_o, max_outliers) entries are read):
+ * Step 2, activation side, for the outlier set given as a bit mask
+ * (mask[ceil(K/32)], bit k%32 of word k/32; only the first max_outliers
+ * outlier columns are gathered):
  *   sx[T], Xq[T][ldq] (ldq >= K bytes, multiple of 16; columns K..ldq-1 and
  *   outlier columns written as 0), Xo[T][ldo] fp16 = X[:, O] with columns
- *   n_o..roundup(n_o,32)-1 written as 0 (ldo multiple of 32, ldo >=
- *   roundup(min(n_o, max_outliers), 32)).
- * mask may be NULL (then it is rebuilt from O inside the kernel).
+ *   n..roundup(n,32)-1 written as 0, n = min(n_o, max_outliers) (ldo a
+ *   multiple of 32, ldo >= roundup(max_outliers, 32)).
  */
-i8mm_status int8_quantize_rows(const void* X, int64_t T, int64_t K,
-                               const int32_t* O, const int32_t* counts, const uint32_t* mask,
+i8mm_status int8_quantize_rows(const void* X, int64_t T, int64_t K, const uint32_t* mask,
                                int64_t max_outliers, int8_t* Xq, int64_t ldq, float* sx,
                                void* Xo, int64_t ldo, hipStream_t stream);
 
 /*
- * Step 2, weight side: Wo[N][ldo] fp16, Wo[j,o] = fp16(fl32(fl32(CB[j,O[o]] *
- * SCB[j]) / 127)) for o < n_o, 0 for n_o <= o < roundup(n_o, 32).
+ * Step 2, weight side, for the outlier set given as a bit mask: Wo[N][ldo]
+ * fp16, Wo[j,o] = fp16(fl32(fl32(CB[j,O[o]] * SCB[j]) / 127)) for o < n,
+ * 0 for n <= o < roundup(n, 32), n = min(n_o, max_outliers).
  */
 i8mm_status int8_outlier_weights(const int8_t* CB, const float* SCB, int64_t N, int64_t K,
-                                 const int32_t* O, const int32_t* counts, int64_t max_outliers,
-                                 void* Wo, int64_t ldo, hipStream_t stream);
+                                 const uint32_t* mask, int64_t max_outliers, void* Wo,
+                                 int64_t ldo, hipStream_t stream);
 
 /*
  * The int8 product of step 2 with its int32 accumulators written out:

@@ -137,10 +137,10 @@ def find_outliers(X: torch.Tensor, threshold: float = DEFAULT_THRESHOLD,
     return O, counts, mask
 
 
-def quantize_rows(X: torch.Tensor, O: torch.Tensor, counts: torch.Tensor,
-                  max_outliers: int, mask: Optional[torch.Tensor] = None,
+def quantize_rows(X: torch.Tensor, mask: torch.Tensor, max_outliers: int,
                   ldq: Optional[int] = None, ldo: Optional[int] = None):
-    """Step 2, activation side: (Xq int8 [T,ldq], sx fp32 [T], Xo fp16 [T,ldo])."""
+    """Step 2, activation side, for an outlier bit mask (uint32 words, int32 tensor):
+    (Xq int8 [T,ldq], sx fp32 [T], Xo fp16 [T,ldo])."""
     _need(X, "X", torch.float16, 2)
     T, K = X.shape
     ldq = ((K + 63) // 64) * 64 if ldq is None else ldq
@@ -149,12 +149,12 @@ def quantize_rows(X: torch.Tensor, O: torch.Tensor, counts: torch.Tensor,
     sx = torch.empty(T, dtype=torch.float32, device=X.device)
     Xo = torch.empty((T, ldo), dtype=torch.float16, device=X.device)
     check("int8_quantize_rows",
-          lib().int8_quantize_rows(_ptr(X), T, K, _ptr(O), _ptr(counts), _ptr(mask), max_outliers,
-                                   _ptr(Xq), ldq, _ptr(sx), _ptr(Xo), ldo, _stream(X)))
+          lib().int8_quantize_rows(_ptr(X), T, K, _ptr(mask), max_outliers, _ptr(Xq), ldq,
+                                   _ptr(sx), _ptr(Xo), ldo, _stream(X)))
     return Xq, sx, Xo
 
 
-def outlier_weights(CB: torch.Tensor, SCB: torch.Tensor, O: torch.Tensor, counts: torch.Tensor,
+def outlier_weights(CB: torch.Tensor, SCB: torch.Tensor, mask: torch.Tensor,
                     max_outliers: int, ldo: Optional[int] = None) -> torch.Tensor:
     """Step 2, weight side: Wo fp16 [N, ldo] = fp16(CB[:, O] * SCB / 127), zero-padded."""
     _need(CB, "CB", torch.int8, 2)
@@ -162,8 +162,8 @@ def outlier_weights(CB: torch.Tensor, SCB: torch.Tensor, O: torch.Tensor, counts
     ldo = max(((max_outliers + 31) // 32) * 32, 32) if ldo is None else ldo
     Wo = torch.empty((N, ldo), dtype=torch.float16, device=CB.device)
     check("int8_outlier_weights",
-          lib().int8_outlier_weights(_ptr(CB), _ptr(SCB), N, K, _ptr(O), _ptr(counts),
-                                     max_outliers, _ptr(Wo), ldo, _stream(CB)))
+          lib().int8_outlier_weights(_ptr(CB), _ptr(SCB), N, K, _ptr(mask), max_outliers,
+                                     _ptr(Wo), ldo, _stream(CB)))
     return Wo
 
 

@@ -42,10 +42,10 @@ SIGNATURES = {
     "int8_find_outliers_scratch_size": (c_size, [c_i64, c_i64]),
     "int8_find_outliers": (c_int, [c_ptr, c_i64, c_i64, c_float, c_ptr, c_ptr, c_ptr, c_i64,
                                    c_ptr, c_size, c_ptr]),
-    "int8_quantize_rows": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_ptr, c_i64, c_ptr, c_i64,
-                                   c_ptr, c_ptr, c_i64, c_ptr]),
-    "int8_outlier_weights": (c_int, [c_ptr, c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_i64, c_ptr,
-                                     c_i64, c_ptr]),
+    "int8_quantize_rows": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_i64, c_ptr, c_i64, c_ptr,
+                                   c_ptr, c_i64, c_ptr]),
+    "int8_outlier_weights": (c_int, [c_ptr, c_ptr, c_i64, c_i64, c_ptr, c_i64, c_ptr, c_i64,
+                                     c_ptr]),
     "int8_gemm_s32": (c_int, [c_ptr, c_i64, c_ptr, c_i64, c_ptr, c_i64, c_i64, c_i64, c_ptr]),
     "i8mm_profile_enable": (c_int, [c_int]),
     "i8mm_profile_read": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),

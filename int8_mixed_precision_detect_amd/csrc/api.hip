@@ -23,16 +23,20 @@ struct DetectGeom {
   int64_t rows_per_block, nrb;
 };
 
-// Row blocks of the detection pass: aim at >= 2048 workgroups, at least 16
-// rows (4 per wave) per workgroup, and a grid.y that HIP accepts.
+// Row blocks of the detection pass: at most 32 (every quantize workgroup
+// ORs them back together), each at least 64 rows so a wave keeps 16 row
+// loads in flight.
 DetectGeom detect_geom(int64_t T, int64_t K) {
-  const int64_t slabs = ceil_div(K > 0 ? K : 1, 512);
-  const int64_t want = ceil_div(2048, slabs);
-  int64_t rpb = round_up(ceil_div(T > 0 ? T : 1, want), 8);
-  if (rpb < 16) rpb = 16;
-  while (ceil_div(T, rpb) > 65535) rpb *= 2;
-  return {rpb, ceil_div(T > 0 ? T : 1, rpb)};
+  (void)K;
+  const int64_t t = T > 0 ? T : 1;
+  int64_t nrb = ceil_div(t, 64);
+  if (nrb > 32) nrb = 32;
+  const int64_t rpb = round_up(ceil_div(t, nrb), 4);
+  return {rpb, ceil_div(t, rpb)};
 }
+
+// O-list capacity (entries) the weight-side workgroups keep in LDS.
+constexpr int64_t kOcap = 8192;
 
 i8mm_status layout_of(int64_t T, int64_t N, int64_t K, int64_t max_o, i8mm_ws_layout* L) {
   if (T < 0 || N < 0 || K < 0 || max_o < 0 || max_o > K) return I8MM_ERR_INVALID_ARG;
@@ -147,18 +151,41 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
 
   int32_t* O = (int32_t*)(w + L.outliers);
   uint32_t* mask = (uint32_t*)(w + L.mask);
+  uint32_t* partial = (uint32_t*)(w + L.partial);
   const DetectGeom g = detect_geom(T, K);
   const bool xvec = (K % 8 == 0) && aligned(X, 16);
-  launch_detect((const _Float16*)X, T, K, threshold, (uint32_t*)(w + L.partial),
-                g.rows_per_block, g.nrb, mask, O, counts, max_outliers, xvec, stream);
+  launch_detect_partial((const _Float16*)X, T, K, threshold, partial, g.rows_per_block, g.nrb,
+                        xvec, stream);
   if (ev) (void)hipEventRecord(ev[1], stream);
 
   int8_t* Xq = (int8_t*)(w + L.xq);
   float* sx = (float*)(w + L.sx);
   _Float16* Xo = (_Float16*)(w + L.xo);
   _Float16* Wo = (_Float16*)(w + L.wo);
-  launch_rowquant((const _Float16*)X, T, K, O, counts, mask, max_outliers, Xq, L.ldq, sx, Xo,
-                  L.ldo, CB, SCB, N, Wo, xvec, stream);
+  PrepArgs pa{};
+  pa.X = (const _Float16*)X;
+  pa.T = T;
+  pa.K = K;
+  pa.partial = partial;
+  pa.nrb = g.nrb;
+  pa.mask_out = mask;
+  pa.O_out = O;
+  pa.counts = counts;
+  pa.max_o = max_outliers;
+  pa.Xq = Xq;
+  pa.ldq = L.ldq;
+  pa.sx = sx;
+  pa.Xo = Xo;
+  pa.ldo = L.ldo;
+  pa.CB = CB;
+  pa.SCB = SCB;
+  pa.N = N;
+  pa.Wo = Wo;
+  pa.small_tail = -1;
+  pa.ocap = max_outliers < kOcap ? max_outliers : kOcap;
+  pa.stage_rows = K <= 16384 && K % 16 == 0 && aligned(CB, 16);
+  pa.vec = xvec;
+  launch_prep(pa, stream);
   if (ev) (void)hipEventRecord(ev[2], stream);
 
   GemmArgs a{};
@@ -215,40 +242,64 @@ i8mm_status int8_find_outliers(const void* X, int64_t T, int64_t K, float thresh
   (void)hipGetLastError();
   const DetectGeom g = detect_geom(T, K);
   const bool xvec = (K % 8 == 0) && aligned(X, 16);
-  launch_detect((const _Float16*)X, T, K, threshold, (uint32_t*)partial, g.rows_per_block, g.nrb,
-                mask, O, counts, max_outliers, xvec, stream);
+  launch_detect_partial((const _Float16*)X, T, K, threshold, (uint32_t*)partial, g.rows_per_block,
+                        g.nrb, xvec, stream);
+  launch_detect_compact((const uint32_t*)partial, g.nrb, K, mask, O, counts, max_outliers, stream);
   return hip_status();
 }
 
-i8mm_status int8_quantize_rows(const void* X, int64_t T, int64_t K, const int32_t* O,
-                               const int32_t* counts, const uint32_t* mask, int64_t max_outliers,
-                               int8_t* Xq, int64_t ldq, float* sx, void* Xo, int64_t ldo,
-                               hipStream_t stream) {
+i8mm_status int8_quantize_rows(const void* X, int64_t T, int64_t K, const uint32_t* mask,
+                               int64_t max_outliers, int8_t* Xq, int64_t ldq, float* sx,
+                               void* Xo, int64_t ldo, hipStream_t stream) {
   if (T <= 0 || K <= 0 || max_outliers < 0 || max_outliers > K) return I8MM_ERR_INVALID_ARG;
   if (T >= kMaxDim || K > kMaxK) return I8MM_ERR_UNSUPPORTED;
   if (ldq < K || ldq % 16 != 0 || ldo < round_up(max_outliers, 32) || ldo % 32 != 0)
     return I8MM_ERR_INVALID_ARG;
-  if (!X || !O || !counts || !Xq || !sx || !Xo || !aligned(X, 2) || !aligned(Xq, 16) ||
-      !aligned(sx, 4) || !aligned(Xo, 2) || (mask && !aligned(mask, 4)))
+  if (!X || !mask || !Xq || !sx || !Xo || !aligned(X, 2) || !aligned(Xq, 16) || !aligned(sx, 4) ||
+      !aligned(Xo, 2) || !aligned(mask, 4))
     return I8MM_ERR_INVALID_ARG;
   (void)hipGetLastError();
-  const bool xvec = (K % 8 == 0) && aligned(X, 16);
-  launch_rowquant((const _Float16*)X, T, K, O, counts, mask, max_outliers, Xq, ldq, sx,
-                  (_Float16*)Xo, ldo, nullptr, nullptr, 0, nullptr, xvec, stream);
+  PrepArgs pa{};
+  pa.X = (const _Float16*)X;
+  pa.T = T;
+  pa.K = K;
+  pa.partial = mask;
+  pa.nrb = 1;
+  pa.max_o = max_outliers;
+  pa.Xq = Xq;
+  pa.ldq = ldq;
+  pa.sx = sx;
+  pa.Xo = (_Float16*)Xo;
+  pa.ldo = ldo;
+  pa.vec = (K % 8 == 0) && aligned(X, 16);
+  launch_prep(pa, stream);
   return hip_status();
 }
 
 i8mm_status int8_outlier_weights(const int8_t* CB, const float* SCB, int64_t N, int64_t K,
-                                 const int32_t* O, const int32_t* counts, int64_t max_outliers,
-                                 void* Wo, int64_t ldo, hipStream_t stream) {
+                                 const uint32_t* mask, int64_t max_outliers, void* Wo,
+                                 int64_t ldo, hipStream_t stream) {
   if (N <= 0 || K <= 0 || max_outliers < 0 || max_outliers > K) return I8MM_ERR_INVALID_ARG;
   if (N >= kMaxDim || K > kMaxK) return I8MM_ERR_UNSUPPORTED;
   if (ldo < round_up(max_outliers, 32) || ldo % 32 != 0) return I8MM_ERR_INVALID_ARG;
-  if (!CB || !SCB || !O || !counts || !Wo || !aligned(SCB, 4) || !aligned(Wo, 2))
+  if (!CB || !SCB || !mask || !Wo || !aligned(SCB, 4) || !aligned(Wo, 2) || !aligned(mask, 4))
     return I8MM_ERR_INVALID_ARG;
   (void)hipGetLastError();
-  launch_rowquant(nullptr, 0, K, O, counts, nullptr, max_outliers, nullptr, 0, nullptr, nullptr,
-                  ldo, CB, SCB, N, (_Float16*)Wo, false, stream);
+  PrepArgs pa{};
+  pa.K = K;
+  pa.partial = mask;
+  pa.nrb = 1;
+  pa.max_o = max_outliers;
+  pa.CB = CB;
+  pa.SCB = SCB;
+  pa.N = N;
+  pa.Wo = (_Float16*)Wo;
+  pa.ldo = ldo;
+  pa.small_tail = -1;
+  pa.ocap = max_outliers < kOcap ? max_outliers : kOcap;
+  pa.stage_rows = K <= 16384 && (K % 16 == 0) && aligned(CB, 16);
+  pa.vec = false;
+  launch_prep(pa, stream);
   return hip_status();
 }
 

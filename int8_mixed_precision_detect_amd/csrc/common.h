@@ -17,15 +17,36 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float h2f(_Float16 h) { return (float)h; }
 
+// n / s with r = fl32(1/s) computed once per row: q0 = n*r, one fused
+// correction step.  For n = fl32(x*127) with fp16 x, |x| <= s, s an fp16
+// value (the absmax codes), and for n = fl32(c*s) / 127 with a code c (the
+// dequantized outlier weights), the result equals the IEEE quotient
+// fl32(n/s) -- checked exhaustively over every such pair by
+// tests/native/quotient_check.c.  Saves the per-element division sequence.
+__device__ __forceinline__ float div_by(float n, float s, float r) {
+#pragma clang fp contract(off)
+  const float q0 = n * r;
+  const float e = __builtin_fmaf(-q0, s, n);
+  return __builtin_fmaf(e, r, q0);
+}
+
 // Absmax code of one value: round half away from zero of the IEEE fp32
 // quotient fl32(x * 127) / s (x*127 is exact for fp16 x); 0 when s == 0.
-// The division is the correctly rounded one (no fast-math in this build).
-__device__ __forceinline__ int8_t absmax_code(float x, float s) {
+// r must be fl32(1/s) (any value when s == 0).
+__device__ __forceinline__ int8_t absmax_code(float x, float s, float r) {
+#pragma clang fp contract(off)
   if (s == 0.0f) return 0;
-  float q = (x * 127.0f) / s;
-  q = __builtin_roundf(q);             // half away from zero
+  float q = div_by(x * 127.0f, s, r);
+  q = __builtin_roundf(q);               // half away from zero
   q = fminf(fmaxf(q, -127.0f), 127.0f);  // no-op for |x| <= s
   return (int8_t)(int)q;
+}
+
+// fp16(fl32(fl32(c * s) / 127)): a dequantized outlier weight
+__device__ __forceinline__ _Float16 dequant_weight(int c, float s) {
+#pragma clang fp contract(off)
+  const float p = (float)c * s;  // exact: <= 8 x 11 significant bits
+  return (_Float16)div_by(p, 127.0f, 1.0f / 127.0f);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

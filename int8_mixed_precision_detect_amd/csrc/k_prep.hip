@@ -2,8 +2,9 @@
 //   k_wquant           weight -> CB/SCB (absmax per output channel)
 //   k_detect_partial   per-row-block column flags |x| >= threshold
 //   k_detect_compact   OR of the row blocks + ordered compaction into O
-//   k_rowquant         masked row absmax, int8 codes, X[:,O] gather, and the
-//                      dequantized outlier weight rows CB[:,O]*SCB/127
+//   k_prep             rebuilds the outlier set, masked row absmax, int8
+//                      codes, X[:,O] gather, dequantized weight rows
+//                      CB[:,O]*SCB/127
 //
 // The method: Hugging Face LLM.int8() summary (agentlenshq.com), section
 // "LLM.int8() の核心アイデア" steps 1-2; absmax rule from its section
@@ -37,6 +38,7 @@ __global__ __launch_bounds__(256) void k_wquant(const _Float16* __restrict__ W, 
     for (int64_t k = threadIdx.x; k < K; k += 256) m = fmaxf(m, fabsf(h2f(row[k])));
   }
   const float s = block_max<256>(m, red);
+  const float r = 1.0f / s;
   if (threadIdx.x == 0) SCB[j] = s;
   if (VEC) {
     const int64_t nc = K / 8;
@@ -45,13 +47,13 @@ __global__ __launch_bounds__(256) void k_wquant(const _Float16* __restrict__ W, 
       v2u packed = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint32_t q = (uint8_t)absmax_code(h2f(v[e]), s);
+        uint32_t q = (uint8_t)absmax_code(h2f(v[e]), s, r);
         packed[e / 4] |= q << (8 * (e % 4));
       }
       *(v2u*)(out + c * 8) = packed;
     }
   } else {
-    for (int64_t k = threadIdx.x; k < K; k += 256) out[k] = absmax_code(h2f(row[k]), s);
+    for (int64_t k = threadIdx.x; k < K; k += 256) out[k] = absmax_code(h2f(row[k]), s, r);
   }
 }
 
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(256) void k_detect_partial(const _Float16* __restri
   if (VEC) {
     if (c0 < K) {
       const _Float16* p = X + c0;
-#pragma unroll 8
+#pragma unroll 16
       for (int64_t r = r0 + w; r < r1; r += 4) {
         v8h v = *(const v8h*)(p + r * K);
 #pragma unroll
@@ -184,126 +186,304 @@ __global__ __launch_bounds__(1024) void k_detect_compact(const uint32_t* __restr
   }
 }
 
-void launch_detect(const _Float16* X, int64_t T, int64_t K, float thr, uint32_t* partial,
-                   int64_t rows_per_block, int64_t nrb, uint32_t* mask, int32_t* O,
-                   int32_t* counts, int64_t max_o, bool vec, hipStream_t st) {
+void launch_detect_partial(const _Float16* X, int64_t T, int64_t K, float thr, uint32_t* partial,
+                           int64_t rows_per_block, int64_t nrb, bool vec, hipStream_t st) {
   const int64_t KW = ceil_div(K, 32);
   dim3 g((unsigned)ceil_div(K, 512), (unsigned)nrb);
   if (vec)
     k_detect_partial<true><<<g, dim3(256), 0, st>>>(X, T, K, rows_per_block, thr, partial, KW);
   else
     k_detect_partial<false><<<g, dim3(256), 0, st>>>(X, T, K, rows_per_block, thr, partial, KW);
+}
+
+void launch_detect_compact(const uint32_t* partial, int64_t nrb, int64_t K, uint32_t* mask,
+                           int32_t* O, int32_t* counts, int64_t max_o, hipStream_t st) {
+  const int64_t KW = ceil_div(K, 32);
   k_detect_compact<<<dim3(1), dim3(1024), (size_t)KW * 4, st>>>(partial, nrb, KW, mask, O,
                                                                  counts, max_o);
 }
 
 // ---------------------------------------------------------------------------
-// Step 2 preparation.  Workgroups [0, nrow) quantize one row of X each:
-// masked absmax -> sx[i], codes -> Xq[i, :] (0 on outlier and pad columns),
-// X[i, O] -> Xo[i, :] (0 on pad columns).  Workgroups [nrow, nrow + ceil(N/8))
-// build 8 rows each of Wo = fp16(fl32(fl32(CB[j, O] * SCB[j]) / 127)).
-// The outlier bit mask lives in LDS (copied from `mask`, or rebuilt from O).
+// Step 2 preparation, one launch.  Every workgroup first rebuilds the outlier
+// set from the detection pass's per-row-block flags: mask word w = OR over
+// the row blocks, and pref[w] = number of outlier columns in words < w (an
+// exclusive scan of popcounts in ascending word order), so the o-th outlier
+// column is the q-th set bit of the word with pref[w] <= o < pref[w+1].
+// Enumerating words in order therefore yields (o, column) pairs ascending
+// and without duplicates -- no sorted list is needed.
+//   workgroup 0 also publishes mask, O and counts (n_o, overflow);
+//   workgroups [0, nrowblk): 4 rows of X each, one row per wave: masked
+//     absmax -> sx, codes -> Xq (0 on outlier and pad columns), X[:, O] ->
+//     Xo (0 on pad columns);
+//   workgroups [nrowblk, nrowblk + nwoblk): 16 output channels each:
+//     Wo[j, o] = fp16(fl32(fl32(CB[j, O[o]] * SCB[j]) / 127)), 0 on pad
+//     columns (skipped when the outlier set has at most small_tail columns).
+// LDS: mask[KW], pref[KW + 1], then (channel workgroups) the O list of up to
+// ocap entries and, when allowed (16-byte aligned CB rows, K <= 16384), one
+// staged CB row per wave.
 // ---------------------------------------------------------------------------
+constexpr int kRowsPerPrepBlock = 4;
+constexpr int kChansPerWoBlock = 16;
+constexpr int kMaxCachedChunks = 24;  // 16-byte chunks of a row a lane keeps in registers
+
 template <bool VEC>
-__global__ __launch_bounds__(256) void k_rowquant(
-    const _Float16* __restrict__ X, int64_t T, int64_t K, const int32_t* __restrict__ O,
-    const int32_t* __restrict__ counts, const uint32_t* __restrict__ mask, int64_t max_o,
-    int8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sx, _Float16* __restrict__ Xo,
-    int64_t ldo, int64_t nrow, const int8_t* __restrict__ CB, const float* __restrict__ SCB,
-    int64_t N, _Float16* __restrict__ Wo) {
-  extern __shared__ uint32_t smask[];
-  __shared__ float red[4];
-  const int tid = threadIdx.x;
-  const int64_t n_o = counts[0];
-  const int64_t n_use = n_o < max_o ? n_o : max_o;
-  const int64_t n_pad = round_up(n_use, 32);
-
-  if ((int64_t)blockIdx.x >= nrow) {
-    // dequantized outlier weight rows
-    const int64_t j = ((int64_t)blockIdx.x - nrow) * 8 + (tid >> 5);
-    if (j >= N) return;
-    const float s = SCB[j];
-    const int8_t* cbrow = CB + j * K;
-    for (int64_t o = tid & 31; o < n_pad; o += 32) {
-      _Float16 v = (_Float16)0.0f;
-      if (o < n_use) {
-        const float p = (float)cbrow[O[o]] * s;  // exact: <= 8 x 11 significant bits
-        v = (_Float16)(p / 127.0f);               // fp32 division, then RNE to fp16
-      }
-      Wo[j * ldo + o] = v;
-    }
-    return;
-  }
-
+__global__ __launch_bounds__(256) void k_prep(
+    const _Float16* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ partial,
+    int64_t nrb, uint32_t* __restrict__ mask_out, int32_t* __restrict__ O_out,
+    int32_t* __restrict__ counts, int64_t max_o, int8_t* __restrict__ Xq, int64_t ldq,
+    float* __restrict__ sx, _Float16* __restrict__ Xo, int64_t ldo, int64_t nrowblk,
+    const int8_t* __restrict__ CB, const float* __restrict__ SCB, int64_t N,
+    _Float16* __restrict__ Wo, int64_t small_tail, int64_t ocap, int stage_rows) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t sm[];
+  __shared__ int32_t wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t KW = ceil_div(K, 32);
-  if (mask) {
-    for (int64_t w = tid; w < KW; w += 256) smask[w] = mask[w];
-  } else {
-    for (int64_t w = tid; w < KW; w += 256) smask[w] = 0u;
-    __syncthreads();
-    for (int64_t o = tid; o < n_use; o += 256) {
-      const int32_t k = O[o];
-      atomicOr(&smask[k >> 5], 1u << (k & 31));
+  uint32_t* smask = sm;
+  int32_t* spref = (int32_t*)(sm + KW);
+
+  // ---- the outlier set: mask words and exclusive prefix of their popcounts
+  // (1) OR the row blocks' words into LDS: coalesced, independent loads,
+  //     8 in flight per thread
+  for (int64_t w = tid; w < KW; w += 256) smask[w] = 0u;
+  __syncthreads();
+  const int64_t tot = nrb * KW;
+  for (int64_t b0 = 0; b0 < tot; b0 += 256 * 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t idx = b0 + u * 256 + tid;
+      v[u] = idx < tot ? partial[idx] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t idx = b0 + u * 256 + tid;
+      if (v[u]) atomicOr(&smask[idx % KW], v[u]);
     }
   }
   __syncthreads();
+  // (2) block-wide exclusive scan of the popcounts; each thread owns a
+  //     contiguous run of words
+  const int64_t per = ceil_div(KW, 256);
+  const int64_t w0 = tid * per, w1 = min(KW, w0 + per);
+  int run = 0;
+  for (int64_t w = w0; w < w1; ++w) run += __popc(smask[w]);
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < wave; ++i) base += wsum[i];
+  const int n_o = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  int acc = base + incl - run;
+  for (int64_t w = w0; w < w1; ++w) {
+    spref[w] = acc;
+    acc += __popc(smask[w]);
+  }
+  if (tid == 0) spref[KW] = n_o;
+  __syncthreads();
+  const int64_t n_use = (int64_t)n_o < max_o ? n_o : max_o;
+  const int64_t n_pad = round_up(n_use, 32);
 
-  const int64_t i = blockIdx.x;
-  const _Float16* row = X + i * K;
-  int8_t* qrow = Xq + i * ldq;
-  float m = 0.0f;
-  if (VEC) {
-    for (int64_t c = tid; c < K / 8; c += 256) {
-      v8h v = *(const v8h*)(row + c * 8);
-      const uint32_t bits = smask[c >> 2] >> (8 * (c & 3));
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (!((bits >> e) & 1u)) m = fmaxf(m, fabsf(h2f(v[e])));
-    }
-  } else {
-    for (int64_t k = tid; k < K; k += 256)
-      if (!((smask[k >> 5] >> (k & 31)) & 1u)) m = fmaxf(m, fabsf(h2f(row[k])));
-  }
-  const float s = block_max<256>(m, red);
-  if (tid == 0) sx[i] = s;
-  if (VEC) {
-    for (int64_t c = tid; c < K / 8; c += 256) {
-      v8h v = *(const v8h*)(row + c * 8);
-      const uint32_t bits = smask[c >> 2] >> (8 * (c & 3));
-      v2u packed = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t q = ((bits >> e) & 1u) ? 0u : (uint32_t)(uint8_t)absmax_code(h2f(v[e]), s);
-        packed[e / 4] |= q << (8 * (e % 4));
+  if (blockIdx.x == 0 && counts) {
+    for (int64_t w = tid; w < KW; w += 256) {
+      uint32_t m = smask[w];
+      if (mask_out) mask_out[w] = m;
+      int64_t o = spref[w];
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1;
+        if (o < max_o) O_out[o] = (int32_t)(w * 32 + b);
+        ++o;
       }
-      *(v2u*)(qrow + c * 8) = packed;
     }
-    for (int64_t k = K + tid; k < ldq; k += 256) qrow[k] = 0;
-  } else {
-    for (int64_t k = tid; k < ldq; k += 256) {
-      int8_t q = 0;
-      if (k < K && !((smask[k >> 5] >> (k & 31)) & 1u)) q = absmax_code(h2f(row[k]), s);
-      qrow[k] = q;
+    if (tid == 0) {
+      counts[0] = n_o;
+      counts[1] = (int64_t)n_o > max_o ? 1 : 0;
+      counts[2] = 0;
+      counts[3] = 0;
     }
   }
-  for (int64_t o = tid; o < n_pad; o += 256)
-    Xo[i * ldo + o] = (o < n_use) ? row[O[o]] : (_Float16)0.0f;
+
+  if ((int64_t)blockIdx.x < nrowblk) {
+    // ---- rows: one per wave, no barrier below this point
+    const int64_t i = (int64_t)blockIdx.x * kRowsPerPrepBlock + wave;
+    if (i >= T) return;
+    const _Float16* row = X + i * K;
+    int8_t* qrow = Xq + i * ldq;
+    float m = 0.0f;
+    if (VEC) {
+      const int64_t nc = K / 8;
+      // chunks lane + 64u stay in registers between the two passes; chunks
+      // beyond kMaxCachedChunks per lane are read again (an L2 hit)
+      v8h cache[kMaxCachedChunks];
+#pragma unroll
+      for (int u = 0; u < kMaxCachedChunks; ++u) {
+        const int64_t c = lane + 64 * u;
+        if (c < nc) cache[u] = *(const v8h*)(row + c * 8);
+      }
+      auto absmax_chunk = [&](int64_t c, v8h v) {
+        const uint32_t bits = smask[c >> 2] >> (8 * (c & 3));
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!((bits >> e) & 1u)) m = fmaxf(m, fabsf(h2f(v[e])));
+      };
+#pragma unroll
+      for (int u = 0; u < kMaxCachedChunks; ++u) {
+        const int64_t c = lane + 64 * u;
+        if (c < nc) absmax_chunk(c, cache[u]);
+      }
+      for (int64_t c = lane + 64 * kMaxCachedChunks; c < nc; c += 64)
+        absmax_chunk(c, *(const v8h*)(row + c * 8));
+      const float s = wave_max(m);
+      const float rs = 1.0f / s;
+      if (lane == 0) sx[i] = s;
+      auto quant_chunk = [&](int64_t c, v8h v) {
+        const uint32_t bits = smask[c >> 2] >> (8 * (c & 3));
+        v2u packed = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t q =
+              ((bits >> e) & 1u) ? 0u : (uint32_t)(uint8_t)absmax_code(h2f(v[e]), s, rs);
+          packed[e / 4] |= q << (8 * (e % 4));
+        }
+        *(v2u*)(qrow + c * 8) = packed;
+      };
+#pragma unroll
+      for (int u = 0; u < kMaxCachedChunks; ++u) {
+        const int64_t c = lane + 64 * u;
+        if (c < nc) quant_chunk(c, cache[u]);
+      }
+      for (int64_t c = lane + 64 * kMaxCachedChunks; c < nc; c += 64)
+        quant_chunk(c, *(const v8h*)(row + c * 8));
+      for (int64_t k = K + lane; k < ldq; k += 64) qrow[k] = 0;
+    } else {
+      for (int64_t k = lane; k < K; k += 64)
+        if (!((smask[k >> 5] >> (k & 31)) & 1u)) m = fmaxf(m, fabsf(h2f(row[k])));
+      const float s = wave_max(m);
+      const float rs = 1.0f / s;
+      if (lane == 0) sx[i] = s;
+      for (int64_t k = lane; k < ldq; k += 64) {
+        int8_t q = 0;
+        if (k < K && !((smask[k >> 5] >> (k & 31)) & 1u)) q = absmax_code(h2f(row[k]), s, rs);
+        qrow[k] = q;
+      }
+    }
+    // X[i, O] -> Xo[i, :]
+    _Float16* xorow = Xo + i * ldo;
+    for (int64_t w = lane; w < KW; w += 64) {
+      uint32_t mb = smask[w];
+      int64_t o = spref[w];
+      while (mb) {
+        const int b = __ffs(mb) - 1;
+        mb &= mb - 1;
+        if (o < n_use) xorow[o] = row[w * 32 + b];
+        ++o;
+      }
+    }
+    for (int64_t o = n_use + lane; o < n_pad; o += 64) xorow[o] = (_Float16)0.0f;
+    return;
+  }
+
+  // ---- dequantized outlier weight rows
+  if (n_use <= small_tail) return;  // the product kernel builds its own
+  const int64_t j0 = ((int64_t)blockIdx.x - nrowblk) * kChansPerWoBlock;
+  if (n_use <= ocap) {
+    // the O list in LDS, then per channel a gather from the CB row (staged
+    // in LDS when wide, so the reads of CB stay coalesced)
+    int32_t* sO = (int32_t*)(spref + KW + 1);
+    for (int64_t w = tid; w < KW; w += 256) {
+      uint32_t mb = smask[w];
+      int64_t o = spref[w];
+      while (mb) {
+        const int b = __ffs(mb) - 1;
+        mb &= mb - 1;
+        if (o < n_use) sO[o] = (int32_t)(w * 32 + b);
+        ++o;
+      }
+    }
+    __syncthreads();
+    // a wide outlier set reads each CB row once, coalesced, into LDS
+    const bool stage = stage_rows && n_use > 64;
+    int8_t* srow = (int8_t*)sm + round_up((2 * KW + 1 + ocap) * 4, 16) + wave * K;
+    for (int r = 0; r < kChansPerWoBlock / 4; ++r) {
+      const int64_t j = j0 + wave * (kChansPerWoBlock / 4) + r;
+      if (j >= N) break;  // uniform across the wave
+      const int8_t* cbrow = CB + j * K;
+      const float sj = SCB[j];
+      if (stage) {  // K % 16 == 0, 16-byte aligned rows, K <= 16384: <= 16 chunks a lane
+        v4i t[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int64_t c = lane + 64 * u;
+          if (c < K / 16) t[u] = *(const v4i*)(cbrow + c * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int64_t c = lane + 64 * u;
+          if (c < K / 16) *(v4i*)(srow + c * 16) = t[u];
+        }
+      }
+      _Float16* worow = Wo + j * ldo;
+      for (int64_t o = lane; o < n_pad; o += 64) {
+        _Float16 v = (_Float16)0.0f;
+        if (o < n_use) {
+          const int8_t c = stage ? srow[sO[o]] : cbrow[sO[o]];
+          v = dequant_weight(c, sj);
+        }
+        worow[o] = v;
+      }
+    }
+  } else {
+    // very large outlier sets: enumerate (o, column) word by word per channel
+    for (int r = 0; r < kChansPerWoBlock / 4; ++r) {
+      const int64_t j = j0 + wave * (kChansPerWoBlock / 4) + r;
+      if (j >= N) break;
+      const int8_t* cbrow = CB + j * K;
+      const float sj = SCB[j];
+      _Float16* worow = Wo + j * ldo;
+      for (int64_t w = lane; w < KW; w += 64) {
+        uint32_t mb = smask[w];
+        int64_t o = spref[w];
+        while (mb) {
+          const int b = __ffs(mb) - 1;
+          mb &= mb - 1;
+          if (o < n_use) worow[o] = dequant_weight(cbrow[w * 32 + b], sj);
+          ++o;
+        }
+      }
+      for (int64_t o = n_use + lane; o < n_pad; o += 64) worow[o] = (_Float16)0.0f;
+    }
+  }
 }
 
-void launch_rowquant(const _Float16* X, int64_t T, int64_t K, const int32_t* O,
-                     const int32_t* counts, const uint32_t* mask, int64_t max_o, int8_t* Xq,
-                     int64_t ldq, float* sx, _Float16* Xo, int64_t ldo, const int8_t* CB,
-                     const float* SCB, int64_t N, _Float16* Wo, bool vec, hipStream_t st) {
-  const int64_t nrow = (Xq != nullptr) ? T : 0;
-  const int64_t nwo = (Wo != nullptr) ? ceil_div(N, 8) : 0;
-  const size_t lds = (size_t)ceil_div(K, 32) * 4;
-  dim3 g((unsigned)(nrow + nwo));
-  if (vec)
-    k_rowquant<true><<<g, dim3(256), lds, st>>>(X, T, K, O, counts, mask, max_o, Xq, ldq, sx, Xo,
-                                                ldo, nrow, CB, SCB, N, Wo);
+size_t prep_lds_bytes(int64_t K, int64_t ocap, bool stage_rows) {
+  const int64_t KW = ceil_div(K, 32);
+  return (size_t)(round_up((2 * KW + 1 + ocap) * 4, 16) + (stage_rows ? 4 * K : 0));
+}
+
+void launch_prep(const PrepArgs& p, hipStream_t st) {
+  const int64_t nrowblk = p.Xq ? ceil_div(p.T, kRowsPerPrepBlock) : 0;
+  const int64_t nwoblk = p.Wo ? ceil_div(p.N, kChansPerWoBlock) : 0;
+  const int64_t ocap = p.Wo ? p.ocap : 0;
+  const bool stage_rows = p.Wo && p.stage_rows;
+  const size_t lds = prep_lds_bytes(p.K, ocap, stage_rows);
+  dim3 g((unsigned)(nrowblk + nwoblk > 0 ? nrowblk + nwoblk : 1));
+  auto go = [&](auto kern) {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    kern<<<g, dim3(256), lds, st>>>(p.X, p.T, p.K, p.partial, p.nrb, p.mask_out, p.O_out,
+                                    p.counts, p.max_o, p.Xq, p.ldq, p.sx, p.Xo, p.ldo, nrowblk,
+                                    p.CB, p.SCB, p.N, p.Wo, p.small_tail, ocap,
+                                    stage_rows ? 1 : 0);
+  };
+  if (p.vec)
+    go(k_prep<true>);
   else
-    k_rowquant<false><<<g, dim3(256), lds, st>>>(X, T, K, O, counts, mask, max_o, Xq, ldq, sx, Xo,
-                                                 ldo, nrow, CB, SCB, N, Wo);
+    go(k_prep<false>);
 }
 
 // Y[i, j] = bias[j] (or 0): the layer with K == 0 (no columns, no outliers).

@@ -104,8 +104,10 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert q(None, 0, 4, None, None, None) == 0
     assert L.int8_gemm_s32(None, 3, None, 4, None, 2, 2, 4, None) == 1   # lda < K
     assert L.int8_find_outliers(None, 4, 8, nan, None, None, None, 8, None, 0, None) == 1
-    assert L.int8_quantize_rows(1 << 20, 4, 8, 1 << 20, 1 << 20, None, 8, 1 << 20, 8,
-                                1 << 20, 1 << 20, 32, None) == 1  # ldq % 16 != 0
+    assert L.int8_quantize_rows(1 << 20, 4, 8, 1 << 20, 8, 1 << 20, 8, 1 << 20, 1 << 20, 32,
+                                None) == 1  # ldq % 16 != 0
+    assert L.int8_outlier_weights(1 << 20, 1 << 20, 4, 8, 1 << 20, 8, 1 << 20, 16,
+                                  None) == 1  # ldo % 32 != 0
 
 
 def test_python_binding_refuses_cpu_tensors():

@@ -94,6 +94,13 @@ def test_find_outliers_overflow(i8):
     assert np.array_equal(host(Og)[:4], Oo[:4].astype(np.int32))
 
 
+def _mask_of(Oo, K):
+    m = np.zeros((K + 31) // 32, dtype=np.uint32)
+    for k in Oo:
+        m[k // 32] |= np.uint32(1) << np.uint32(k % 32)
+    return m.view(np.int32)
+
+
 @pytest.mark.parametrize("case", list(range(len(SHAPES) + 4)))
 def test_quantize_rows_bitexact(i8, case):
     X, thr = list(_detect_cases())[case]
@@ -105,15 +112,13 @@ def test_quantize_rows_bitexact(i8, case):
     Xqo, sxo = O.quantize_rows(X, Oo)
     Xoo = X[:, Oo]
     n = len(Oo)
-    mo = K
-    O_dev = dev(np.concatenate([Oo.astype(np.int32), np.zeros(1, np.int32)]))
-    counts = dev(np.array([n, 0, 0, 0], dtype=np.int32))
     say("quantize_rows", T, K, n)
-    for use_mask in (False, True):
-        mask = None
-        if use_mask:
+    for source in ("oracle mask", "gpu mask"):
+        if source == "gpu mask":
             _, _, mask = i8.find_outliers(dev(X), thr)
-        Xq, sx, Xo = i8.quantize_rows(dev(X), O_dev, counts, mo, mask=mask)
+        else:
+            mask = dev(_mask_of(Oo, K))
+        Xq, sx, Xo = i8.quantize_rows(dev(X), mask, K)
         Xq, sx, Xo = host(Xq), host(sx), host(Xo)
         assert np.array_equal(sx.view(np.uint32), sxo.view(np.uint32))
         assert np.array_equal(Xq[:, :K], Xqo)
@@ -123,18 +128,34 @@ def test_quantize_rows_bitexact(i8, case):
         assert np.all(Xo[:, n:npad].view(np.uint16) == 0)
 
 
-@pytest.mark.parametrize("case", list(range(len(SHAPES))))
+def test_quantize_rows_capped(i8):
+    """max_outliers below n_o: only the first max_outliers outlier columns are gathered."""
+    d = make_random_case(63, 40, 256, 8, n_planted=10)
+    X = d["X"]
+    Oo = O.find_outliers(X, 6.0)
+    say("quantize_rows capped")
+    Xq, sx, Xo = i8.quantize_rows(dev(X), dev(_mask_of(Oo, 256)), 4)
+    Xqo, sxo = O.quantize_rows(X, Oo)
+    assert np.array_equal(host(Xq)[:, :256], Xqo)
+    assert np.array_equal(host(Xo)[:, :4].view(np.uint16), X[:, Oo[:4]].view(np.uint16))
+
+
+@pytest.mark.parametrize("case", list(range(len(SHAPES) + 2)))
 def test_outlier_weights_bitexact(i8, case):
-    (N, K), W = list(_weight_cases())[case]
-    rng = np.random.default_rng(70 + case)
-    n = int(rng.integers(0, K + 1))
+    if case < len(SHAPES):
+        (N, K), W = list(_weight_cases())[case]
+        rng = np.random.default_rng(70 + case)
+        n = int(rng.integers(0, K + 1))
+    else:  # wide outlier sets, where CB rows are staged in LDS
+        rng = np.random.default_rng(80 + case)
+        N, K = 300, 2048 if case == len(SHAPES) else 12288
+        W = make_weight(rng, N, K, 0.02)
+        n = int(K * 0.23)
     Oo = np.sort(rng.choice(K, size=n, replace=False)).astype(np.int64)
     CBo, SCBo = O.quantize_weight(W)
     _, Woo = O.gather_outliers(np.zeros((1, K), np.float16), CBo, SCBo, Oo)
     say("outlier_weights", N, K, n)
-    Wo = host(i8.outlier_weights(dev(CBo), dev(SCBo),
-                                 dev(np.concatenate([Oo.astype(np.int32), [0]]).astype(np.int32)),
-                                 dev(np.array([n, 0, 0, 0], np.int32)), K))
+    Wo = host(i8.outlier_weights(dev(CBo), dev(SCBo), dev(_mask_of(Oo, K)), K))
     npad = ((n + 31) // 32) * 32
     assert np.array_equal(Wo[:, :n].view(np.uint16), Woo.view(np.uint16))
     assert np.all(Wo[:, n:npad].view(np.uint16) == 0)
