@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define I8MM_ABI_VERSION 1
+#define I8MM_ABI_VERSION 2
 
 typedef enum {
   I8MM_OK = 0,
@@ -90,15 +90,12 @@ typedef struct {
   size_t counts;   /* int32[4]: n_o (true count), overflow flag, 0, 0          */
   size_t outliers; /* int32[max_outliers]: outlier columns O, ascending       */
   size_t mask;     /* uint32[ceil(K/32)]: bit k set iff column k is an outlier */
-  size_t partial;  /* uint32[n_row_blocks][ceil(K/32)]: per-row-block flags    */
   size_t sx;       /* fp32[T]: row scales (absmax over non-outlier columns)    */
   size_t xq;       /* int8[T][ldq]: quantized X, outlier and pad columns 0     */
   size_t xo;       /* fp16[T][ldo]: X[:, O], zero-padded to ldo                */
   size_t wo;       /* fp16[N][ldo]: fp16(CB[:, O] * SCB / 127), zero-padded    */
-  size_t p;        /* fp32[T][N] outlier product, only when max_outliers > 96  */
   int64_t ldq;     /* row pitch of xq in bytes (K rounded up to 64)            */
   int64_t ldo;     /* row pitch of xo and wo in elements (max_outliers up to 32) */
-  int64_t n_row_blocks;
   size_t total;    /* bytes the workspace must hold                            */
 } i8mm_ws_layout;
 
@@ -153,19 +150,16 @@ i8mm_status int8_linear_status(const void* ws, int32_t* n_outliers, hipStream_t 
 /* ---- stage entry points (the same kernels the forward runs) -------------- */
 
 /*
- * Step 1 alone.  Writes counts[0] = n_o, counts[1] = overflow (n_o >
- * max_outliers), O[0 .. min(n_o, max_outliers)) ascending, and the bit mask
- * mask[ceil(K/32)] (bit k%32 of word k/32).  `partial` is scratch of
- * int8_find_outliers_scratch_size(T, K) bytes.  counts: int32[4].
- * (The forward runs the same per-row-block detection kernel; its compaction
- * happens inside the step-2 kernel, which publishes the same mask, O and
- * counts into the workspace.)
+ * Step 1 alone.  Writes the bit mask mask[ceil(K/32)] (bit k%32 of word
+ * k/32 set iff some |X[i,k]| >= threshold), counts[0] = n_o, counts[1] =
+ * overflow (n_o > max_outliers), counts[2..3] = 0, and O[0 .. min(n_o,
+ * max_outliers)) ascending.  counts: int32[4].  T, K > 0.
+ * (The forward runs the same detection kernel; the list O and the counts
+ * are then produced by the step-2 kernel from the same mask.)
  */
-size_t int8_find_outliers_scratch_size(int64_t T, int64_t K);
 i8mm_status int8_find_outliers(const void* X, int64_t T, int64_t K, float threshold,
                                int32_t* O, int32_t* counts, uint32_t* mask,
-                               int64_t max_outliers, void* partial, size_t partial_bytes,
-                               hipStream_t stream);
+                               int64_t max_outliers, hipStream_t stream);
 
 /*
  * Step 2, activation side, for the outlier set given as a bit mask

@@ -129,11 +129,9 @@ def find_outliers(X: torch.Tensor, threshold: float = DEFAULT_THRESHOLD,
     O = torch.empty(max(mo, 1), dtype=torch.int32, device=X.device)
     counts = torch.empty(4, dtype=torch.int32, device=X.device)
     mask = torch.empty(max((K + 31) // 32, 1), dtype=torch.int32, device=X.device)
-    nbytes = lib().int8_find_outliers_scratch_size(T, K)
-    part = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=X.device)
     check("int8_find_outliers",
           lib().int8_find_outliers(_ptr(X), T, K, float(threshold), _ptr(O), _ptr(counts),
-                                   _ptr(mask), mo, _ptr(part), part.numel(), _stream(X)))
+                                   _ptr(mask), mo, _stream(X)))
     return O, counts, mask
 
 

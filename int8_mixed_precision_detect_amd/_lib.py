@@ -23,9 +23,9 @@ c_float = ctypes.c_float
 
 class WsLayout(ctypes.Structure):
     _fields_ = [
-        ("counts", c_size), ("outliers", c_size), ("mask", c_size), ("partial", c_size),
-        ("sx", c_size), ("xq", c_size), ("xo", c_size), ("wo", c_size), ("p", c_size),
-        ("ldq", c_i64), ("ldo", c_i64), ("n_row_blocks", c_i64), ("total", c_size),
+        ("counts", c_size), ("outliers", c_size), ("mask", c_size), ("sx", c_size),
+        ("xq", c_size), ("xo", c_size), ("wo", c_size), ("ldq", c_i64), ("ldo", c_i64),
+        ("total", c_size),
     ]
 
 
@@ -39,9 +39,8 @@ SIGNATURES = {
     "int8_linear_forward": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_i64, c_ptr, c_float,
                                     c_ptr, c_ptr, c_size, c_i64, c_ptr]),
     "int8_linear_status": (c_int, [c_ptr, ctypes.POINTER(ctypes.c_int32), c_ptr]),
-    "int8_find_outliers_scratch_size": (c_size, [c_i64, c_i64]),
     "int8_find_outliers": (c_int, [c_ptr, c_i64, c_i64, c_float, c_ptr, c_ptr, c_ptr, c_i64,
-                                   c_ptr, c_size, c_ptr]),
+                                   c_ptr]),
     "int8_quantize_rows": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_i64, c_ptr, c_i64, c_ptr,
                                    c_ptr, c_i64, c_ptr]),
     "int8_outlier_weights": (c_int, [c_ptr, c_ptr, c_i64, c_i64, c_ptr, c_i64, c_ptr, c_i64,

@@ -19,33 +19,16 @@ constexpr int64_t kMaxK = (int64_t)1 << 18;    // LDS copy of the outlier bit ma
 
 inline bool aligned(const void* p, uintptr_t a) { return (((uintptr_t)p) & (a - 1)) == 0; }
 
-struct DetectGeom {
-  int64_t rows_per_block, nrb;
-};
-
-// Row blocks of the detection pass: at most 32 (every quantize workgroup
-// ORs them back together), each at least 64 rows so a wave keeps 16 row
-// loads in flight.
-DetectGeom detect_geom(int64_t T, int64_t K) {
-  (void)K;
-  const int64_t t = T > 0 ? T : 1;
-  int64_t nrb = ceil_div(t, 64);
-  if (nrb > 32) nrb = 32;
-  const int64_t rpb = round_up(ceil_div(t, nrb), 4);
-  return {rpb, ceil_div(t, rpb)};
-}
-
-// O-list capacity (entries) the weight-side workgroups keep in LDS.
-constexpr int64_t kOcap = 8192;
+// O-list capacity (entries) the step-2 workgroups keep in LDS; larger
+// outlier sets are enumerated from the mask instead.
+constexpr int64_t kOcap = 4096;
 
 i8mm_status layout_of(int64_t T, int64_t N, int64_t K, int64_t max_o, i8mm_ws_layout* L) {
   if (T < 0 || N < 0 || K < 0 || max_o < 0 || max_o > K) return I8MM_ERR_INVALID_ARG;
   if (T >= kMaxDim || N >= kMaxDim || K > kMaxK) return I8MM_ERR_UNSUPPORTED;
-  const DetectGeom g = detect_geom(T, K);
   const int64_t KW = ceil_div(K, 32);
   L->ldq = round_up(K, 64);
   L->ldo = round_up(max_o, 32);
-  L->n_row_blocks = g.nrb;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -55,12 +38,10 @@ i8mm_status layout_of(int64_t T, int64_t N, int64_t K, int64_t max_o, i8mm_ws_la
   L->counts = take(16);
   L->outliers = take((size_t)(max_o > 0 ? max_o : 1) * 4);
   L->mask = take((size_t)(KW > 0 ? KW : 1) * 4);
-  L->partial = take((size_t)(g.nrb * (KW > 0 ? KW : 1)) * 4);
   L->sx = take((size_t)T * 4);
   L->xq = take((size_t)T * (size_t)L->ldq);
   L->xo = take((size_t)T * (size_t)L->ldo * 2);
   L->wo = take((size_t)N * (size_t)L->ldo * 2);
-  L->p = take(max_o > kSmallTail ? (size_t)T * (size_t)N * 4 : 0);
   L->total = off;
   return I8MM_OK;
 }
@@ -151,11 +132,8 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
 
   int32_t* O = (int32_t*)(w + L.outliers);
   uint32_t* mask = (uint32_t*)(w + L.mask);
-  uint32_t* partial = (uint32_t*)(w + L.partial);
-  const DetectGeom g = detect_geom(T, K);
   const bool xvec = (K % 8 == 0) && aligned(X, 16);
-  launch_detect_partial((const _Float16*)X, T, K, threshold, partial, g.rows_per_block, g.nrb,
-                        xvec, stream);
+  launch_detect((const _Float16*)X, T, K, threshold, mask, nullptr, xvec, stream);
   if (ev) (void)hipEventRecord(ev[1], stream);
 
   int8_t* Xq = (int8_t*)(w + L.xq);
@@ -166,9 +144,7 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   pa.X = (const _Float16*)X;
   pa.T = T;
   pa.K = K;
-  pa.partial = partial;
-  pa.nrb = g.nrb;
-  pa.mask_out = mask;
+  pa.mask = mask;
   pa.O_out = O;
   pa.counts = counts;
   pa.max_o = max_outliers;
@@ -181,9 +157,7 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   pa.SCB = SCB;
   pa.N = N;
   pa.Wo = Wo;
-  pa.small_tail = -1;
   pa.ocap = max_outliers < kOcap ? max_outliers : kOcap;
-  pa.stage_rows = K <= 16384 && K % 16 == 0 && aligned(CB, 16);
   pa.vec = xvec;
   launch_prep(pa, stream);
   if (ev) (void)hipEventRecord(ev[2], stream);
@@ -205,7 +179,6 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   a.max_o = max_outliers;
   a.bias = (const _Float16*)bias;
   a.Y = (_Float16*)Y;
-  a.P = (float*)(w + L.p);
   const hipError_t ge = gemm_i8_supported(a) ? launch_gemm_i8_fused(a, stream)
                                              : launch_gemm_fused(a, stream);
   if (ge != hipSuccess) return I8MM_ERR_HIP;
@@ -223,28 +196,19 @@ i8mm_status int8_linear_status(const void* ws, int32_t* n_outliers, hipStream_t 
   return c[1] ? I8MM_ERR_OUTLIER_OVERFLOW : I8MM_OK;
 }
 
-size_t int8_find_outliers_scratch_size(int64_t T, int64_t K) {
-  if (T < 0 || K < 0) return 0;
-  const DetectGeom g = detect_geom(T, K);
-  return (size_t)(g.nrb * (ceil_div(K, 32) > 0 ? ceil_div(K, 32) : 1)) * 4;
-}
-
 i8mm_status int8_find_outliers(const void* X, int64_t T, int64_t K, float threshold, int32_t* O,
                                int32_t* counts, uint32_t* mask, int64_t max_outliers,
-                               void* partial, size_t partial_bytes, hipStream_t stream) {
+                               hipStream_t stream) {
   if (isnan(threshold) || !(threshold > 0.0f)) return I8MM_ERR_INVALID_ARG;
   if (T <= 0 || K <= 0 || max_outliers < 0 || max_outliers > K) return I8MM_ERR_INVALID_ARG;
   if (T >= kMaxDim || K > kMaxK) return I8MM_ERR_UNSUPPORTED;
-  if (!X || !O || !counts || !mask || !partial || !aligned(X, 2) || !aligned(O, 4) ||
-      !aligned(counts, 4) || !aligned(mask, 4) || !aligned(partial, 4))
+  if (!X || !O || !counts || !mask || !aligned(X, 2) || !aligned(O, 4) || !aligned(counts, 4) ||
+      !aligned(mask, 4))
     return I8MM_ERR_INVALID_ARG;
-  if (partial_bytes < int8_find_outliers_scratch_size(T, K)) return I8MM_ERR_WORKSPACE;
   (void)hipGetLastError();
-  const DetectGeom g = detect_geom(T, K);
   const bool xvec = (K % 8 == 0) && aligned(X, 16);
-  launch_detect_partial((const _Float16*)X, T, K, threshold, (uint32_t*)partial, g.rows_per_block,
-                        g.nrb, xvec, stream);
-  launch_detect_compact((const uint32_t*)partial, g.nrb, K, mask, O, counts, max_outliers, stream);
+  launch_detect((const _Float16*)X, T, K, threshold, mask, nullptr, xvec, stream);
+  launch_compact(mask, K, O, counts, max_outliers, stream);
   return hip_status();
 }
 
@@ -263,14 +227,14 @@ i8mm_status int8_quantize_rows(const void* X, int64_t T, int64_t K, const uint32
   pa.X = (const _Float16*)X;
   pa.T = T;
   pa.K = K;
-  pa.partial = mask;
-  pa.nrb = 1;
+  pa.mask = mask;
   pa.max_o = max_outliers;
   pa.Xq = Xq;
   pa.ldq = ldq;
   pa.sx = sx;
   pa.Xo = (_Float16*)Xo;
   pa.ldo = ldo;
+  pa.ocap = max_outliers < kOcap ? max_outliers : kOcap;
   pa.vec = (K % 8 == 0) && aligned(X, 16);
   launch_prep(pa, stream);
   return hip_status();
@@ -287,17 +251,14 @@ i8mm_status int8_outlier_weights(const int8_t* CB, const float* SCB, int64_t N, 
   (void)hipGetLastError();
   PrepArgs pa{};
   pa.K = K;
-  pa.partial = mask;
-  pa.nrb = 1;
+  pa.mask = mask;
   pa.max_o = max_outliers;
   pa.CB = CB;
   pa.SCB = SCB;
   pa.N = N;
   pa.Wo = (_Float16*)Wo;
   pa.ldo = ldo;
-  pa.small_tail = -1;
   pa.ocap = max_outliers < kOcap ? max_outliers : kOcap;
-  pa.stage_rows = K <= 16384 && (K % 16 == 0) && aligned(CB, 16);
   pa.vec = false;
   launch_prep(pa, stream);
   return hip_status();

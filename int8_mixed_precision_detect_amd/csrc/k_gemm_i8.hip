@@ -1,15 +1,16 @@
-// The int8 product of the LLM.int8() layer, tuned for gfx950 (16-byte
-// aligned operands), and the fp16 product over a large outlier set.
+// The products of the LLM.int8() layer, tuned for gfx950 (16-byte aligned
+// operands).
 //
 // Step 2 of "LLM.int8() の核心アイデア" (Hugging Face summary page) multiplies
 // the non-outlier dims in int8 and the outlier dims in fp16; step 3
 // dequantizes the int8 result and adds the fp16 one.  Here:
 //
 //   k_gemm_i8<..., MODE_I32>    C = Xq . CB^T (exact int32)
-//   k_gemm_i8<..., MODE_FUSED>  Y = fp16(acc*sx*SCB/127^2 + Xo.Wo^T + bias)
-//   k_gemm_i8<..., MODE_F16>    P = Xo . Wo^T in fp32, only when the outlier
-//                                   set is too large for the fused epilogue
-//                                   (more than kSmallTail columns)
+//   k_gemm_i8<..., MODE_FUSED>  Y = fp16(acc*sx*SCB/127^2 + Xo.Wo^T + bias):
+//       the int8 slices of K, then the accumulators are scaled to fp32 in
+//       place and the fp16 outlier slices (Xo/Wo rows, 64 halves a slice)
+//       stream through the same LDS pipeline into them with
+//       v_mfma_f32_16x16x32_f16, then bias and one fp16 rounding.
 //
 // Workgroup: a BM x BN output tile (channels x tokens) split over waves of
 // WM x WN, each an array of 16 x 16 v_mfma_i32_16x16x64_i8 blocks.  K is
@@ -33,6 +34,8 @@
 // applied on the global side: lane i fetches the chunk that belongs at its
 // LDS position.  Chunks past the end of K read as zeros (their offset points
 // past the buffer's range), so any K that is a multiple of 16 is exact.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -40,7 +43,9 @@ namespace i8mm {
 
 namespace {
 
-constexpr int MODE_I32 = 0, MODE_FUSED = 1, MODE_F16 = 2;
+constexpr int MODE_I32 = 0, MODE_FUSED = 1;
+using I8Slices = std::false_type;
+using F16Slices = std::true_type;
 
 template <int KB>
 __device__ __forceinline__ int swz(int r) {
@@ -90,17 +95,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / NWN) * WM, wn0 = (wave % NWN) * WN;
 
-  // the outlier-product launch only has work for a large outlier set
-  int64_t nt_tail = 0;  // 32-column (64-byte) k-steps of the outlier operands
-  if constexpr (MODE != MODE_I32) {
-    const int64_t n_o = a.counts[0];
-    const int64_t n_use = n_o < a.max_o ? n_o : a.max_o;
-    nt_tail = ceil_div(n_use, 32);
-    if constexpr (MODE == MODE_F16) {
-      if (nt_tail <= kSmallTail / 32) return;
-    }
-  }
-
   // tile order: workgroups are dealt to the 8 XCDs round-robin; give each XCD
   // a contiguous run of tiles, consecutive tiles sharing one weight tile.
   const int64_t tiles_m = ceil_div(a.N, BM), tiles_n = ceil_div(a.T, BN);
@@ -117,20 +111,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   __amdgpu_buffer_rsrc_t rsA, rsB;
   uint32_t voff[PW];
-  int kc[PW];
+  // a lane's chunk within its row: rows of a piece start at multiples of
+  // RPP (8 or 16), so the swizzle of row rr depends only on the lane
+  const int kc = ((lane % CPR) ^ swz<KB>(lane / CPR)) * 16;
   auto setup = [&](const char* A, int64_t ldab, int64_t rowsA, const char* B, int64_t ldbb,
                    int64_t rowsB) {
     rsA = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(rowsA * ldab), 0x00020000);
     rsB = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(rowsB * ldbb), 0x00020000);
+    // an opaque copy of the lane index: the row indices of a later setup
+    // (the outlier operands index the same channels) are recomputed rather
+    // than kept live across the K loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
       const int j = wv * PW + u;  // piece: RPP rows of A, then of B (wave-uniform)
       const bool isA = j < ACH;
-      const int rr = (isA ? j : j - ACH) * RPP + lane / CPR;
-      const int c = (lane % CPR) ^ swz<KB>(rr);
+      const int rr = (isA ? j : j - ACH) * RPP + ln / CPR;
+      static_assert(RPP % 8 == 0, "swizzle period");
       const int64_t g = isA ? min(m0 + rr, a.N - 1) : min(n0 + rr, a.T - 1);
-      voff[u] = (uint32_t)(g * (isA ? ldab : ldbb) + c * 16);
-      kc[u] = c * 16;
+      voff[u] = (uint32_t)(g * (isA ? ldab : ldbb) + kc);
     }
   };
   auto lds_dst = [&](int buf, int u) {
@@ -147,7 +147,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     } else {
 #pragma unroll
       for (int u = 0; u < PW; ++u) {
-        const uint32_t vo = (k0 + kc[u] < Kb) ? voff[u] : 0x80000000u;
+        const uint32_t vo = (k0 + kc < Kb) ? voff[u] : 0x80000000u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wv * PW + u < ACH ? rsA : rsB, lds_dst(buf, u), 16,
                                                  vo, (int)k0, 0, 0);
       }
@@ -167,8 +167,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
 #pragma unroll
     for (int j = 0; j < NI; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  auto mfma = [&](int i, int j, v4i x, v4i y) {
-    if constexpr (MODE == MODE_F16) {
+  auto mma = [&](auto f16, int i, int j, v4i x, v4i y) {
+    if constexpr (decltype(f16)::value) {
       acc[i][j] = __builtin_bit_cast(
           v4i, __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x),
                                                       __builtin_bit_cast(v8h, y),
@@ -178,34 +178,51 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     }
   };
   // the MFMAs of one slice; the other waves of the SIMD cover LDS latency
-  auto compute = [&](int buf) {
+  auto compute = [&](auto f16, int buf) {
     const char* As = lds + buf * STAGE;
     const char* Bs = As + BM * KB;
 #pragma unroll
     for (int h = 0; h < KS; ++h) {
-      v4i fa[MI], fb[NI];
+      if constexpr (MI * NI <= 32) {
+        // small wave tile: the compiler schedules the fragment reads freely
+        v4i fa[MI], fb[NI];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) fa[i] = *(const v4i*)(As + frag_off(wm0 + i * 16, h));
+        for (int i = 0; i < MI; ++i) fa[i] = *(const v4i*)(As + frag_off(wm0 + i * 16, h));
 #pragma unroll
-      for (int j = 0; j < NI; ++j) fb[j] = *(const v4i*)(Bs + frag_off(wn0 + j * 16, h));
+        for (int j = 0; j < NI; ++j) fb[j] = *(const v4i*)(Bs + frag_off(wn0 + j * 16, h));
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NI; ++j) mfma(i, j, fa[i], fb[j]);
+          for (int j = 0; j < NI; ++j) mma(f16, i, j, fa[i], fb[j]);
+      } else {
+        // wide wave tile: token fragments once per k-step, channel fragments
+        // one ahead of their NI MFMAs, in a fixed order, so that the live
+        // fragments stay at NI + 2 registers of 4
+        v4i fb[NI], fa0, fa1;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) fb[j] = *(const v4i*)(Bs + frag_off(wn0 + j * 16, h));
+        fa0 = *(const v4i*)(As + frag_off(wm0, h));
+        __builtin_amdgcn_sched_group_barrier(0x100, NI + 1, 0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          if (i + 1 < MI) {
+            fa1 = *(const v4i*)(As + frag_off(wm0 + (i + 1) * 16, h));
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+#pragma unroll
+          for (int j = 0; j < NI; ++j) mma(f16, i, j, fa0, fb[j]);
+          __builtin_amdgcn_sched_group_barrier(0x008, NI, 0);
+          fa0 = fa1;
+        }
+      }
     }
   };
 
-  int64_t Kb;
-  if constexpr (MODE == MODE_F16) {
-    setup((const char*)a.Wo, a.ldo * 2, a.N, (const char*)a.Xo, a.ldo * 2, a.T);
-    Kb = nt_tail * 64;
-  } else {
-    setup((const char*)a.A, a.lda, a.N, (const char*)a.B, a.ldb, a.T);
-    Kb = a.K;
-  }
-  const int64_t nk = ceil_div(Kb, KB);
-
-  if (nk > 0) {
+  // K loop over Kb bytes of the operands set up last: S slices in flight,
+  // one barrier per slice.  LDS must be free of earlier readers on entry.
+  auto run = [&](auto f16, int64_t Kb) {
+    const int64_t nk = ceil_div(Kb, KB);
+    if (nk <= 0) return;
 #pragma unroll
     for (int s = 0; s < S; ++s)
       if (s < nk) issue(s, s * KB, Kb);
@@ -220,9 +237,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       // done with slice kt-1, whose buffer is refilled with slice kt-1+S
       __builtin_amdgcn_s_barrier();
       if (kt >= 1 && kt - 1 + S < nk) issue((int)((kt - 1) % S), (kt - 1 + S) * KB, Kb);
-      compute((int)(kt % S));
+      compute(f16, (int)(kt % S));
+      // keeps the epilogue's loads (scales, bias) below the loop instead of
+      // hoisted above it, where they would hold registers throughout
+      asm volatile("" ::: "memory");
     }
-  }
+  };
+
+  setup((const char*)a.A, a.lda, a.N, (const char*)a.B, a.ldb, a.T);
+  run(I8Slices{}, a.K);
 
   const int lrow = 4 * (lane >> 4);  // first of the 4 channels a lane holds
   const int lcol = lane & 15;        // token within a 16-wide block
@@ -246,102 +269,49 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
         }
       }
     }
-  } else if constexpr (MODE == MODE_F16) {
-    const bool pvec = ((a.N & 3) == 0) && ((((uintptr_t)a.P) & 15) == 0);
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int64_t f = m0 + wm0 + i * 16 + lrow;
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int64_t t = n0 + wn0 + j * 16 + lcol;
-        if (t >= a.T) continue;
-        float* dst = a.P + t * a.N + f;
-        const v4f v = __builtin_bit_cast(v4f, acc[i][j]);
-        if (pvec && f + 3 < a.N) {
-          *(v4f*)dst = v;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (f + r < a.N) dst[r] = v[r];
-        }
-      }
-    }
   } else {
     // ---- fused epilogue ----
-    // small outlier sets: stage Xo/Wo (<= kSmallTail columns) in LDS and run
-    // the fp16 MFMAs per output block into a fresh accumulator; large ones:
-    // the fp32 product P was written by the MODE_F16 launch before.
-    const bool small = nt_tail <= kSmallTail / 32;
-    const int64_t Kt = nt_tail * 64;        // bytes of a tail row
-    const int ntl = (int)ceil_div(Kt, KB);  // tail slices
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();  // every wave is done with the int8 slices
-    if (small && nt_tail > 0) {
-      static_assert(S * KB >= kSmallTail * 2, "the small tail must fit the slice buffers");
-      setup((const char*)a.Wo, a.ldo * 2, a.N, (const char*)a.Xo, a.ldo * 2, a.T);
-      for (int s = 0; s < S; ++s)
-        if (s < ntl) issue(s, s * KB, Kt);
-      wait_vm<0>();
-      __builtin_amdgcn_s_barrier();
-    }
+    const int64_t n_o = a.counts[0];
+    const int64_t n_use = n_o < a.max_o ? n_o : a.max_o;
+    const int64_t Kt = round_up(n_use, 32) * 2;  // bytes of an Xo / Wo row in use
     float sxv[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int64_t t = n0 + wn0 + j * 16 + lcol;
       sxv[j] = (t < a.T) ? a.sx[t] : 0.0f;
     }
-    const bool yvec = ((a.N & 3) == 0) && ((((uintptr_t)a.Y) & 7) == 0);
-    const bool pvec = ((a.N & 3) == 0) && ((((uintptr_t)a.P) & 15) == 0);
-    float scv[MI][4], bvv[MI][4];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t f = m0 + wm0 + i * 16 + lrow + r;
-        const bool in = f < a.N;
-        scv[i][r] = in ? a.SCB[f] * (1.0f / 16129.0f) : 0.0f;
-        bvv[i][r] = (a.bias && in) ? h2f(a.bias[f]) : 0.0f;
+        const float sc = f < a.N ? a.SCB[f] * (1.0f / 16129.0f) : 0.0f;
+        // int32 accumulator -> fp32 acc * sx * SCB / 127^2, in place
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+          acc[i][j][r] = __builtin_bit_cast(int, (float)acc[i][j][r] * (sxv[j] * sc));
       }
-    v8h ta[MI];
-    if (small && nt_tail == 1) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i) ta[i] = *(const v8h*)(lds + frag_off(wm0 + i * 16, 0));
+    if (Kt > 0) {
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();  // every wave is done with the int8 slices
+      setup((const char*)a.Wo, a.ldo * 2, a.N, (const char*)a.Xo, a.ldo * 2, a.T);
+      run(F16Slices{}, Kt);
     }
+    const bool yvec = ((a.N & 3) == 0) && ((((uintptr_t)a.Y) & 7) == 0);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int64_t t = n0 + wn0 + j * 16 + lcol;
-      v8h tb = {};
-      if (small && nt_tail == 1) tb = *(const v8h*)(lds + BM * KB + frag_off(wn0 + j * 16, 0));
+    for (int i = 0; i < MI; ++i) {
+      const int64_t f = m0 + wm0 + i * 16 + lrow;  // 4 consecutive channels
+      float bv[4];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int64_t f = m0 + wm0 + i * 16 + lrow;
-        v4f p = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (small) {
-          if (nt_tail == 1) {
-            p = __builtin_amdgcn_mfma_f32_16x16x32_f16(ta[i], tb, p, 0, 0, 0);
-          } else {
-            for (int64_t q = 0; q < nt_tail; ++q) {  // 64-byte k-steps of the tail
-              const char* base = lds + (int)(q / KS) * STAGE;
-              const int h = (int)(q % KS);
-              const v8h xa = *(const v8h*)(base + frag_off(wm0 + i * 16, h));
-              const v8h xb = *(const v8h*)(base + BM * KB + frag_off(wn0 + j * 16, h));
-              p = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, xb, p, 0, 0, 0);
-            }
-          }
-        } else if (t < a.T) {
-          const float* src = a.P + t * a.N + f;
-          if (pvec && f + 3 < a.N) {
-            p = *(const v4f*)src;
-          } else {
+      for (int r = 0; r < 4; ++r) bv[r] = (a.bias && f + r < a.N) ? h2f(a.bias[f + r]) : 0.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = (f + r < a.N) ? src[r] : 0.0f;
-          }
-        }
+      for (int j = 0; j < NI; ++j) {
+        const int64_t t = n0 + wn0 + j * 16 + lcol;
         if (t >= a.T) continue;
+        const v4f v = __builtin_bit_cast(v4f, acc[i][j]);
         v4h y;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          y[r] = (_Float16)((float)acc[i][j][r] * (sxv[j] * scv[i][r]) + p[r] + bvv[i][r]);
+        for (int r = 0; r < 4; ++r) y[r] = (_Float16)(v[r] + bv[r]);
         _Float16* dst = a.Y + t * a.N + f;
         if (yvec && f + 3 < a.N) {
           *(v4h*)dst = y;
@@ -356,10 +326,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-#ifndef I8MM_CFG
-#define I8MM_CFG 20
-#endif
-
 namespace {
 template <int BM, int BN, int WM, int WN, int S, int KB, int MODE>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
@@ -373,27 +339,42 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// tile configurations: channels x tokens per workgroup, per wave, slices in
-// flight, slice bytes per row.  Configuration 20 (256 x 256, 8 waves of
-// 64 x 128, two 128-byte slices in flight, 128 KB of LDS) measured fastest
-// on the first feed-forward shapes (13B: 242 us against 275 us for the
-// 64-byte, four-slice configuration 3).
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// Tile configurations (channels x tokens per workgroup, per wave, slices
+// in flight, slice bytes per row), one workgroup per CU (LDS-bound):
+//   A: 256 x 256, 8 waves of 64 x 128, two 128-byte slices (128 KB LDS)
+//   B: 320 x 256, 8 waves of 80 x 128, two 128-byte slices (144 KB LDS)
+// The workgroups run in waves of one per CU, so a launch costs about
+// ceil(tiles / CUs) times the time of one tile.  The host takes the
+// configuration with the smaller ceil(tiles / CUs) * tile area (ties go to
+// A): on the 13B-scale layer (20480 x 2048 outputs) A needs 640 tiles, 2.5
+// waves, and B 512 tiles, 2 full waves.
 template <int MODE>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
-#if I8MM_CFG == 3
-  return launch_cfg<256, 256, 64, 128, 4, 64, MODE>(a, st);
-#elif I8MM_CFG == 20
+#ifdef I8MM_CFG
+#if I8MM_CFG == 20
   return launch_cfg<256, 256, 64, 128, 2, 128, MODE>(a, st);
-#elif I8MM_CFG == 21
-  return launch_cfg<256, 128, 64, 64, 3, 128, MODE>(a, st);
-#elif I8MM_CFG == 22
-  return launch_cfg<256, 256, 128, 64, 2, 128, MODE>(a, st);
-#elif I8MM_CFG == 23
-  return launch_cfg<128, 256, 64, 64, 3, 128, MODE>(a, st);
-#elif I8MM_CFG == 24
-  return launch_cfg<256, 256, 64, 64, 2, 128, MODE>(a, st);
+#elif I8MM_CFG == 25
+  return launch_cfg<320, 256, 80, 128, 2, 128, MODE>(a, st);
+#elif I8MM_CFG == 26
+  return launch_cfg<320, 256, 160, 64, 2, 128, MODE>(a, st);
 #else
 #error "unknown I8MM_CFG"
+#endif
+#else
+  const int64_t cus = cu_count();
+  auto cost = [&](int64_t bm, int64_t bn) {
+    return ceil_div(ceil_div(a.N, bm) * ceil_div(a.T, bn), cus) * bm * bn;
+  };
+  if (cost(320, 256) < cost(256, 256)) return launch_cfg<320, 256, 80, 128, 2, 128, MODE>(a, st);
+  return launch_cfg<256, 256, 64, 128, 2, 128, MODE>(a, st);
 #endif
 }
 }  // namespace
@@ -412,9 +393,6 @@ hipError_t launch_gemm_i8_s32(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm_i8_fused(const GemmArgs& a, hipStream_t st) {
-  // the fp16 product of a large outlier set first (returns at once otherwise)
-  hipError_t e = launch_mode<MODE_F16>(a, st);
-  if (e != hipSuccess) return e;
   return launch_mode<MODE_FUSED>(a, st);
 }
 

@@ -8,25 +8,23 @@ namespace i8mm {
 
 void launch_wquant(const _Float16* W, int64_t N, int64_t K, int8_t* CB, float* SCB, bool vec,
                    hipStream_t st);
-// Outlier detection: per-row-block column flags, and (for the stage entry
-// point) their compaction into mask, O and counts.
-void launch_detect_partial(const _Float16* X, int64_t T, int64_t K, float thr, uint32_t* partial,
-                           int64_t rows_per_block, int64_t nrb, bool vec, hipStream_t st);
-void launch_detect_compact(const uint32_t* partial, int64_t nrb, int64_t K, uint32_t* mask,
-                           int32_t* O, int32_t* counts, int64_t max_o, hipStream_t st);
+// Outlier detection: zero mask[ceil(K/32)] (and counts[4] when given), then
+// OR the column flags |x| >= thr of kDetectRows-row blocks into it.
+constexpr int64_t kDetectRows = 32;
+void launch_detect(const _Float16* X, int64_t T, int64_t K, float thr, uint32_t* mask,
+                   int32_t* counts, bool vec, hipStream_t st);
+// mask -> ascending O (first max_o entries), counts {n_o, overflow, 0, 0}.
+void launch_compact(const uint32_t* mask, int64_t K, int32_t* O, int32_t* counts, int64_t max_o,
+                    hipStream_t st);
 
-// Step 2 preparation in one launch (see k_prep): rebuilds the outlier set
-// from `partial` (nrb row blocks of ceil(K/32) words; a final mask is nrb 1),
-// optionally publishes mask/O/counts, quantizes rows (Xq != null) and builds
-// the dequantized outlier weights (Wo != null; only when the outlier set is
-// larger than small_tail).
+// Step 2 preparation in one launch (see k_prep): the outlier set from the
+// mask, optionally published as O/counts (counts != null), rows of X
+// quantized (Xq != null) and the dequantized outlier weights (Wo != null).
 struct PrepArgs {
   const _Float16* X;
   int64_t T, K;
-  const uint32_t* partial;
-  int64_t nrb;
-  uint32_t* mask_out;  // published by workgroup 0 when counts != null
-  int32_t* O_out;
+  const uint32_t* mask;
+  int32_t* O_out;  // written by workgroup 0 when counts != null
   int32_t* counts;
   int64_t max_o;
   int8_t* Xq;
@@ -38,12 +36,10 @@ struct PrepArgs {
   const float* SCB;
   int64_t N;
   _Float16* Wo;
-  int64_t small_tail;  // Wo is built only when n_use > small_tail
-  int64_t ocap;        // O-list capacity in LDS for the Wo workgroups
-  bool stage_rows;     // stage CB rows in LDS for the Wo gather
-  bool vec;            // 16-byte aligned rows of X (K % 8 == 0)
+  int64_t ocap;  // outlier-list capacity in LDS (entries)
+  bool vec;      // 16-byte aligned rows of X (K % 8 == 0)
 };
-size_t prep_lds_bytes(int64_t K, int64_t ocap, bool stage_rows);
+size_t prep_lds_bytes(int64_t K, int64_t ocap);
 void launch_prep(const PrepArgs& p, hipStream_t st);
 void launch_fill_bias(_Float16* Y, int64_t T, int64_t N, const _Float16* bias, int32_t* counts,
                       hipStream_t st);
@@ -67,15 +63,7 @@ struct GemmArgs {
   _Float16* Y;
   // int32 output instead of the epilogue
   int32_t* C;
-  // fp32 [T][N] product over a large outlier set (more than kSmallTail
-  // columns); only read or written in that case
-  float* P;
 };
-
-// Outlier columns the aligned fused kernel handles inside its epilogue
-// (3 slices of 32, staged in LDS); beyond that a separate fp16 launch writes
-// P first.
-constexpr int64_t kSmallTail = 96;
 
 // Any shape and alignment: register-staged, byte-granular loads.
 hipError_t launch_gemm_fused(const GemmArgs& a, hipStream_t st);

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.i8mm_abi_version() == 1
+    assert L.i8mm_abi_version() == 2
     for code, name in [(0, b"I8MM_OK"), (1, b"I8MM_ERR_INVALID_ARG"), (2, b"I8MM_ERR_WORKSPACE"),
                        (3, b"I8MM_ERR_UNSUPPORTED"), (4, b"I8MM_ERR_HIP"),
                        (5, b"I8MM_ERR_OUTLIER_OVERFLOW")]:
@@ -60,9 +60,8 @@ def test_workspace_layout(L):
         assert L.int8_linear_workspace_layout(T, N, K, mo, ctypes.byref(lay)) == 0
         regions = [("counts", 16), ("outliers", max(mo, 1) * 4),
                    ("mask", max(math.ceil(K / 32), 1) * 4),
-                   ("partial", lay.n_row_blocks * max(math.ceil(K / 32), 1) * 4),
                    ("sx", T * 4), ("xq", T * lay.ldq), ("xo", T * lay.ldo * 2),
-                   ("wo", N * lay.ldo * 2), ("p", T * N * 4 if mo > 96 else 0)]
+                   ("wo", N * lay.ldo * 2)]
         end = 0
         for name, size in regions:
             off = getattr(lay, name)
@@ -103,7 +102,8 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     assert q(None, -1, 4, None, None, None) == 1
     assert q(None, 0, 4, None, None, None) == 0
     assert L.int8_gemm_s32(None, 3, None, 4, None, 2, 2, 4, None) == 1   # lda < K
-    assert L.int8_find_outliers(None, 4, 8, nan, None, None, None, 8, None, 0, None) == 1
+    assert L.int8_find_outliers(None, 4, 8, nan, None, None, None, 8, None) == 1
+    assert L.int8_find_outliers(1 << 20, 4, 8, 6.0, None, 1 << 20, 1 << 20, 8, None) == 1
     assert L.int8_quantize_rows(1 << 20, 4, 8, 1 << 20, 8, 1 << 20, 8, 1 << 20, 1 << 20, 32,
                                 None) == 1  # ldq % 16 != 0
     assert L.int8_outlier_weights(1 << 20, 1 << 20, 4, 8, 1 << 20, 8, 1 << 20, 16,

@@ -118,6 +118,22 @@ def test_zero_rows_and_threshold_tie(i8):
     _full_check(i8, X, W, d["bias"], 6.0, "zero rows / tie")
 
 
+def test_wide_channel_tile(i8):
+    # 2048 x 20380 outputs take the 320-channel tile configuration; the last
+    # channel tile is ragged (220 of 320 rows)
+    d = make_random_case(906, 2048, 256, 20380, n_planted=5, row_frac=0.3)
+    _full_check(i8, d["X"], d["W"], d["bias"], 6.0, "320-channel tiles 2048x256x20380")
+
+
+@pytest.mark.parametrize("T,K,N,thr", [(64, 2048, 200, 3.0), (48, 8192, 96, 2.0)])
+def test_wide_outlier_sets(i8, T, K, N, thr):
+    # ~16% and ~89% of the columns are outliers; the second set is larger
+    # than the outlier list step 2 keeps in LDS, so it takes the path that
+    # enumerates the mask instead
+    d = make_random_case(T * 7 + K, T, K, N, n_planted=0, bias=True)
+    _full_check(i8, d["X"], d["W"], d["bias"], thr, f"wide set {T}x{K}x{N} thr={thr}")
+
+
 def test_k_zero_gives_bias(i8):
     import torch
     T, N = 5, 7

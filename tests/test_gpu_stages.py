@@ -162,7 +162,10 @@ def test_outlier_weights_bitexact(i8, case):
 
 
 GEMM_SHAPES = [(16, 64, 64), (300, 517, 1024), (257, 300, 1000), (1, 1, 1), (5, 7, 24),
-               (513, 257, 2048), (64, 1024, 4160), (2, 3, 12288)]
+               (513, 257, 2048), (64, 1024, 4160), (2, 3, 12288),
+               # large enough for the 320-channel tile (2 full waves of
+               # workgroups instead of 2.5), with a ragged last channel tile
+               (2048, 20380, 320)]
 
 
 @pytest.mark.parametrize("T,N,K", GEMM_SHAPES)
