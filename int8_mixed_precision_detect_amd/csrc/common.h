@@ -17,6 +17,14 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float h2f(_Float16 h) { return (float)h; }
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// A raw buffer resource over `bytes` bytes at p: loads at offsets >= bytes
+// return 0 without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)bytes, 0x00020000);
+}
+#endif
+
 // n / s with r = fl32(1/s) computed once per row: q0 = n*r, one fused
 // correction step.  For n = fl32(x*127) with fp16 x, |x| <= s, s an fp16
 // value (the absmax codes), and for n = fl32(c*s) / 127 with a code c (the
@@ -30,16 +38,55 @@ __device__ __forceinline__ float div_by(float n, float s, float r) {
   return __builtin_fmaf(e, r, q0);
 }
 
-// Absmax code of one value: round half away from zero of the IEEE fp32
-// quotient fl32(x * 127) / s (x*127 is exact for fp16 x); 0 when s == 0.
-// r must be fl32(1/s) (any value when s == 0).
-__device__ __forceinline__ int8_t absmax_code(float x, float s, float r) {
+// Reciprocal for the absmax codes of a row with scale s: fl32(1/s), and 0
+// for s == 0 (every code of such a row is 0, with no per-element test).
+__device__ __forceinline__ float code_recip(float s) { return s > 0.0f ? 1.0f / s : 0.0f; }
+
+// Absmax code of one value, |x| <= s, r = code_recip(s): round half away
+// from zero of the IEEE fp32 quotient fl32(x * 127) / s (x*127 is exact for
+// fp16 x).  The quotient comes from div_by; the rounding is an fp32 add of
+// +-0.5 and a truncating conversion.  On its own that add can round (just
+// below 0.5, for instance), but for every quotient these codes can produce
+// -- every fp16 pair |x| <= s -- it equals the exact rule, as checked
+// exhaustively by tests/native/quotient_check.c.  |q| <= 127, so no clamp.
+__device__ __forceinline__ int absmax_code(float x, float s, float r) {
 #pragma clang fp contract(off)
-  if (s == 0.0f) return 0;
-  float q = div_by(x * 127.0f, s, r);
-  q = __builtin_roundf(q);               // half away from zero
-  q = fminf(fmaxf(q, -127.0f), 127.0f);  // no-op for |x| <= s
-  return (int8_t)(int)q;
+  const float q = div_by(x * 127.0f, s, r);
+  return (int)(q + __builtin_copysignf(0.5f, q));
+}
+
+// Codes of 8 fp16 values (|v[e]| <= s), packed little-endian into 8 bytes.
+__device__ __forceinline__ v2u absmax_codes8(v8h v, float s, float r) {
+  v2u out;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      word |= ((uint32_t)absmax_code((float)v[4 * w + b], s, r) & 0xffu) << (8 * b);
+    out[w] = word;
+  }
+  return out;
+}
+
+// v with the elements whose bit is set in the low 8 bits of `bits` zeroed
+__device__ __forceinline__ v8h zero_masked8(v8h v, uint32_t bits) {
+  if (bits & 0xffu) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((bits >> e) & 1u) v[e] = (_Float16)0.0f;
+  }
+  return v;
+}
+
+// max |v[e]| in fp16 (exact), as float
+__device__ __forceinline__ float absmax8(v8h v) {
+  typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+  v2h m = __builtin_elementwise_abs(v2h{v[0], v[1]});
+#pragma unroll
+  for (int e = 2; e < 8; e += 2)
+    m = __builtin_elementwise_max(m, __builtin_elementwise_abs(v2h{v[e], v[e + 1]}));
+  return fmaxf((float)m[0], (float)m[1]);
 }
 
 // fp16(fl32(fl32(c * s) / 127)): a dequantized outlier weight

@@ -29,31 +29,20 @@ __global__ __launch_bounds__(256) void k_wquant(const _Float16* __restrict__ W, 
   float m = 0.0f;
   if (VEC) {
     const int64_t nc = K / 8;
-    for (int64_t c = threadIdx.x; c < nc; c += 256) {
-      v8h v = *(const v8h*)(row + c * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(h2f(v[e])));
-    }
+    for (int64_t c = threadIdx.x; c < nc; c += 256) m = fmaxf(m, absmax8(*(const v8h*)(row + c * 8)));
   } else {
     for (int64_t k = threadIdx.x; k < K; k += 256) m = fmaxf(m, fabsf(h2f(row[k])));
   }
   const float s = block_max<256>(m, red);
-  const float r = 1.0f / s;
+  const float r = code_recip(s);
   if (threadIdx.x == 0) SCB[j] = s;
   if (VEC) {
     const int64_t nc = K / 8;
-    for (int64_t c = threadIdx.x; c < nc; c += 256) {
-      v8h v = *(const v8h*)(row + c * 8);
-      v2u packed = {0u, 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t q = (uint8_t)absmax_code(h2f(v[e]), s, r);
-        packed[e / 4] |= q << (8 * (e % 4));
-      }
-      *(v2u*)(out + c * 8) = packed;
-    }
+    for (int64_t c = threadIdx.x; c < nc; c += 256)
+      *(v2u*)(out + c * 8) = absmax_codes8(*(const v8h*)(row + c * 8), s, r);
   } else {
-    for (int64_t k = threadIdx.x; k < K; k += 256) out[k] = absmax_code(h2f(row[k]), s, r);
+    for (int64_t k = threadIdx.x; k < K; k += 256)
+      out[k] = (int8_t)absmax_code(h2f(row[k]), s, r);
   }
 }
 
@@ -137,12 +126,12 @@ void launch_detect(const _Float16* X, int64_t T, int64_t K, float thr, uint32_t*
 // spref[w] <= o < spref[w+1], so enumerating words in order yields O
 // ascending, without duplicates and without sorting.
 // ---------------------------------------------------------------------------
+// The same, with smask[KW] already filled by the calling threads (not yet
+// synchronized).
 template <int NT>
-__device__ int outlier_scan(const uint32_t* __restrict__ mask, int64_t KW, uint32_t* smask,
-                            int32_t* spref, int32_t* wsum) {
+__device__ int outlier_scan_lds(int64_t KW, uint32_t* smask, int32_t* spref, int32_t* wsum) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int64_t w = tid; w < KW; w += NT) smask[w] = mask[w];
   __syncthreads();
   const int64_t per = ceil_div(KW, NT);
   const int64_t w0 = tid * per, w1 = min(KW, w0 + per);
@@ -170,6 +159,13 @@ __device__ int outlier_scan(const uint32_t* __restrict__ mask, int64_t KW, uint3
   if (tid == 0) spref[KW] = n_o;
   __syncthreads();
   return n_o;
+}
+
+template <int NT>
+__device__ int outlier_scan(const uint32_t* __restrict__ mask, int64_t KW, uint32_t* smask,
+                            int32_t* spref, int32_t* wsum) {
+  for (int64_t w = threadIdx.x; w < KW; w += NT) smask[w] = mask[w];
+  return outlier_scan_lds<NT>(KW, smask, spref, wsum);
 }
 
 // O[o] for o < cap (ascending), into `dst` (global or LDS)
@@ -219,9 +215,10 @@ void launch_compact(const uint32_t* mask, int64_t K, int32_t* O, int32_t* counts
 // from the mask (outlier_scan) and, when it has at most ocap columns, the
 // list O in LDS.
 //   workgroup 0 also publishes O and counts (n_o, overflow);
-//   workgroups [0, T): one row of X each: masked absmax -> sx, codes -> Xq
-//     (0 on outlier and pad columns), X[:, O] -> Xo (0 on pad columns);
-//   workgroups [T, T + ceil(N/64)): 64 output channels each:
+//   workgroups [0, R = ceil(T/RPB)): RPB rows of X each, 256/RPB threads a
+//     row: masked absmax -> sx, codes -> Xq (0 on outlier and pad columns),
+//     X[:, O] -> Xo (0 on pad columns);
+//   workgroups [R, R + ceil(N/16)): 16 output channels each:
 //     Wo[j, o] = fp16(fl32(fl32(CB[j, O[o]] * SCB[j]) / 127)), 0 on pad.
 // A row workgroup issues its loads of X before rebuilding the outlier set
 // (they do not depend on it), so the two latencies overlap.  O is
@@ -230,42 +227,74 @@ void launch_compact(const uint32_t* mask, int64_t K, int32_t* O, int32_t* counts
 // Outlier sets beyond ocap fall back to enumerating the mask per row.
 // LDS: mask[KW], pref[KW + 1], O[ocap].
 // ---------------------------------------------------------------------------
-constexpr int kChansPerWoBlock = 64;
-constexpr int kCachedChunks = 8;  // 16-byte chunks of a row a thread keeps in registers
+constexpr int kChansPerWoBlock = 16;
+constexpr int kMaskWords = 2;  // mask words a thread requests before the row
+// One row per workgroup measured best across the first-FF shapes (2 and 4
+// rows per workgroup: 13B-scale 12.2 / 10.9 us against 11.8 us, 175B-scale
+// 51 / 60 us against 46 us, 32-token decode 10 / 16 us against 7 us).
+constexpr int kRowsPerPrepBlock = 1;
 
-template <bool VEC>
+// RPB rows of X per workgroup, 256 / RPB threads (whole waves) per row
+template <bool VEC, int RPB>
 __global__ __launch_bounds__(256) void k_prep(
     const _Float16* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ mask,
     int32_t* __restrict__ O_out, int32_t* __restrict__ counts, int64_t max_o,
     int8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sx, _Float16* __restrict__ Xo,
     int64_t ldo, int64_t nrowblk, const int8_t* __restrict__ CB, const float* __restrict__ SCB,
     int64_t N, _Float16* __restrict__ Wo, int64_t ocap) {
+  // The body uses amdgcn-only types (buffer resources); the host pass only
+  // needs the kernel's signature to emit its launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int TPR = 256 / RPB;                        // threads per row
+  constexpr int kCachedChunks = RPB == 1 ? 4 : RPB == 2 ? 6 : 10;  // chunks a thread keeps
   extern __shared__ __attribute__((aligned(16))) uint32_t sm[];
   __shared__ int32_t wsum[4];
   __shared__ float red[4];
   const int tid = threadIdx.x;
+  const int rt = tid % TPR;  // thread within its row
   const int64_t KW = ceil_div(K, 32);
   uint32_t* smask = sm;
   int32_t* spref = (int32_t*)(sm + KW);
   int32_t* sO = spref + KW + 1;
 
-  // rows: X loads first
+  // The mask words are requested first and the row's X chunks right after:
+  // loads complete in order, so the scan waits only for the mask while the
+  // X loads are still in flight.
+  // (Buffer loads: out-of-range offsets read 0 and touch no memory, so every
+  // workgroup runs the same straight-line loads -- the channel workgroups
+  // with an empty row range -- and the compiler can wait for the mask alone.)
+  const __amdgpu_buffer_rsrc_t rmask = make_rsrc(mask, (uint32_t)(KW * 4));
+  uint32_t mw[kMaskWords];
+#pragma unroll
+  for (int u = 0; u < kMaskWords; ++u)
+    mw[u] = __builtin_amdgcn_raw_buffer_load_b32(rmask, (tid + 256 * u) * 4, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);  // keep the mask loads ahead of the row's
   const bool row_block = (int64_t)blockIdx.x < nrowblk;
-  const int64_t i = blockIdx.x;
-  const _Float16* row = X + i * K;
+  // the row of this thread's wave (wave-uniform: a row spans whole waves)
+  const int64_t i = (int64_t)blockIdx.x * RPB + __builtin_amdgcn_readfirstlane(tid / TPR);
+  const bool row_ok = row_block && i < T;
+  const _Float16* row = X + (row_ok ? i * K : 0);
   const int64_t nc = K / 8;
   v8h cache[kCachedChunks];
-  if (VEC && row_block) {
-    // chunks tid + 256u stay in registers between the two passes; chunks
+  if (VEC) {
+    // chunks rt + TPR*u stay in registers between the two passes; chunks
     // beyond kCachedChunks per thread are read again (an L2 hit)
+    const __amdgpu_buffer_rsrc_t rrow = make_rsrc(row, row_ok ? (uint32_t)(nc * 16) : 0u);
 #pragma unroll
-    for (int u = 0; u < kCachedChunks; ++u) {
-      const int64_t c = tid + 256 * u;
-      if (c < nc) cache[u] = *(const v8h*)(row + c * 8);
-    }
+    for (int u = 0; u < kCachedChunks; ++u)
+      cache[u] = __builtin_bit_cast(
+          v8h, __builtin_amdgcn_raw_buffer_load_b128(rrow, (rt + TPR * u) * 16, 0, 0));
   }
-
-  const int n_o = outlier_scan<256>(mask, KW, smask, spref, wsum);
+  // unconditional stores (a conditional one lets the compiler sink its load
+  // behind the row's): words past the mask are 0 and land in smask[KW], the
+  // first prefix slot, which the scan writes after its first barrier
+#pragma unroll
+  for (int u = 0; u < kMaskWords; ++u) {
+    const int64_t w = tid + 256 * u;
+    smask[w < KW ? w : KW] = mw[u];
+  }
+  for (int64_t w = tid + 256 * kMaskWords; w < KW; w += 256) smask[w] = mask[w];
+  const int n_o = outlier_scan_lds<256>(KW, smask, spref, wsum);
   const int64_t n_use = (int64_t)n_o < max_o ? n_o : max_o;
   const int64_t n_pad = round_up(n_use, 32);
   const bool listed = n_use <= ocap;
@@ -282,75 +311,85 @@ __global__ __launch_bounds__(256) void k_prep(
   __syncthreads();
 
   if (row_block) {
-    // ---- one row of X
-    int8_t* qrow = Xq + i * ldq;
+    // ---- RPB rows of X, TPR threads each
+    // max over the TPR threads of a row (every thread of the block calls it)
+    auto row_max = [&](float v) {
+      v = wave_max(v);
+      if constexpr (TPR > 64) {
+        constexpr int WPR = TPR / 64;
+        const int w = tid >> 6;
+        if ((tid & 63) == 0) red[w] = v;
+        __syncthreads();
+        const int w0 = w - w % WPR;
+        v = red[w0];
+#pragma unroll
+        for (int q = 1; q < WPR; ++q) v = fmaxf(v, red[w0 + q]);
+      }
+      return v;
+    };
+    int8_t* qrow = Xq + (row_ok ? i : 0) * ldq;
     float m = 0.0f;
     if (VEC) {
-      auto absmax_chunk = [&](int64_t c, v8h v) {
-        const uint32_t bits = smask[c >> 2] >> (8 * (c & 3));
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (!((bits >> e) & 1u)) m = fmaxf(m, fabsf(h2f(v[e])));
-      };
+      // outlier columns are zeroed in the chunk first (rare); then the row
+      // absmax and the codes need no per-element test
+      auto chunk_bits = [&](int64_t c) { return smask[c >> 2] >> (8 * (c & 3)); };
 #pragma unroll
       for (int u = 0; u < kCachedChunks; ++u) {
-        const int64_t c = tid + 256 * u;
-        if (c < nc) absmax_chunk(c, cache[u]);
-      }
-      for (int64_t c = tid + 256 * kCachedChunks; c < nc; c += 256)
-        absmax_chunk(c, *(const v8h*)(row + c * 8));
-      const float s = block_max<256>(m, red);
-      const float rs = 1.0f / s;
-      if (tid == 0) sx[i] = s;
-      auto quant_chunk = [&](int64_t c, v8h v) {
-        const uint32_t bits = smask[c >> 2] >> (8 * (c & 3));
-        v2u packed = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t q =
-              ((bits >> e) & 1u) ? 0u : (uint32_t)(uint8_t)absmax_code(h2f(v[e]), s, rs);
-          packed[e / 4] |= q << (8 * (e % 4));
+        const int64_t c = rt + TPR * u;
+        if (c < nc) {
+          cache[u] = zero_masked8(cache[u], chunk_bits(c));
+          m = fmaxf(m, absmax8(cache[u]));
         }
-        *(v2u*)(qrow + c * 8) = packed;
-      };
+      }
+      if (row_ok)
+        for (int64_t c = rt + TPR * kCachedChunks; c < nc; c += TPR)
+          m = fmaxf(m, absmax8(zero_masked8(*(const v8h*)(row + c * 8), chunk_bits(c))));
+      const float s = row_max(m);
+      if (!row_ok) return;
+      const float rs = code_recip(s);
+      if (rt == 0) sx[i] = s;
 #pragma unroll
       for (int u = 0; u < kCachedChunks; ++u) {
-        const int64_t c = tid + 256 * u;
-        if (c < nc) quant_chunk(c, cache[u]);
+        const int64_t c = rt + TPR * u;
+        if (c < nc) *(v2u*)(qrow + c * 8) = absmax_codes8(cache[u], s, rs);
       }
-      for (int64_t c = tid + 256 * kCachedChunks; c < nc; c += 256)
-        quant_chunk(c, *(const v8h*)(row + c * 8));
-      for (int64_t k = K + tid; k < ldq; k += 256) qrow[k] = 0;
+      for (int64_t c = rt + TPR * kCachedChunks; c < nc; c += TPR)
+        *(v2u*)(qrow + c * 8) =
+            absmax_codes8(zero_masked8(*(const v8h*)(row + c * 8), chunk_bits(c)), s, rs);
+      for (int64_t k = K + rt; k < ldq; k += TPR) qrow[k] = 0;
     } else {
-      for (int64_t k = tid; k < K; k += 256)
-        if (!((smask[k >> 5] >> (k & 31)) & 1u)) m = fmaxf(m, fabsf(h2f(row[k])));
-      const float s = block_max<256>(m, red);
-      const float rs = 1.0f / s;
-      if (tid == 0) sx[i] = s;
-      for (int64_t k = tid; k < ldq; k += 256) {
+      if (row_ok)
+        for (int64_t k = rt; k < K; k += TPR)
+          if (!((smask[k >> 5] >> (k & 31)) & 1u)) m = fmaxf(m, fabsf(h2f(row[k])));
+      const float s = row_max(m);
+      if (!row_ok) return;
+      const float rs = code_recip(s);
+      if (rt == 0) sx[i] = s;
+      for (int64_t k = rt; k < ldq; k += TPR) {
         int8_t q = 0;
-        if (k < K && !((smask[k >> 5] >> (k & 31)) & 1u)) q = absmax_code(h2f(row[k]), s, rs);
+        if (k < K && !((smask[k >> 5] >> (k & 31)) & 1u))
+          q = (int8_t)absmax_code(h2f(row[k]), s, rs);
         qrow[k] = q;
       }
     }
     // X[i, O] -> Xo[i, :]
     _Float16* xorow = Xo + i * ldo;
     if (listed) {
-      for (int64_t o0 = 0; o0 < n_pad; o0 += 4 * 256) {
+      for (int64_t o0 = 0; o0 < n_pad; o0 += 4 * TPR) {
         _Float16 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int64_t o = o0 + u * 256 + tid;
+          const int64_t o = o0 + u * TPR + rt;
           v[u] = o < n_use ? row[sO[o]] : (_Float16)0.0f;
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int64_t o = o0 + u * 256 + tid;
+          const int64_t o = o0 + u * TPR + rt;
           if (o < n_pad) xorow[o] = v[u];
         }
       }
     } else {
-      for (int64_t w = tid; w < KW; w += 256) {
+      for (int64_t w = rt; w < KW; w += TPR) {
         uint32_t mb = smask[w];
         int64_t o = spref[w];
         while (mb && o < n_use) {
@@ -359,7 +398,7 @@ __global__ __launch_bounds__(256) void k_prep(
           xorow[o++] = row[w * 32 + b];
         }
       }
-      for (int64_t o = n_use + tid; o < n_pad; o += 256) xorow[o] = (_Float16)0.0f;
+      for (int64_t o = n_use + rt; o < n_pad; o += TPR) xorow[o] = (_Float16)0.0f;
     }
     return;
   }
@@ -369,27 +408,43 @@ __global__ __launch_bounds__(256) void k_prep(
   const int64_t nch = min((int64_t)kChansPerWoBlock, N - j0);
   if (n_pad == 0 || nch <= 0) return;
   if (listed) {
-    // (channel, o) pairs flattened over the workgroup, 4 gathers in flight
-    const uint32_t np = (uint32_t)n_pad, total = (uint32_t)(nch * n_pad);
-    for (uint32_t p0 = 0; p0 < total; p0 += 4 * 256) {
-      int8_t c[4];
-      float sj[4];
+    // per wave: items (channel r, chunk u of 64 outputs), wave-uniform, so
+    // the channel's row address and scale stay scalar; a lane gathers
+    // output o = 64u + lane; kGather items in flight
+    constexpr int kGather = 4;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int64_t nu = ceil_div(n_pad, 64);
+    const int64_t nr = ceil_div(nch - wave, 4);  // channels wave, wave+4, ...
+    const int64_t items = nr * nu;
+    int64_t r0 = 0, u0 = 0;  // (channel step, chunk) of the batch's first item
+    for (int64_t q0 = 0; q0 < items; q0 += kGather) {
+      int64_t rg[kGather], ug[kGather];
+      int64_t rr = r0, uu = u0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t p = p0 + u * 256 + tid;
-        const uint32_t ch = p / np, o = p - ch * np;
-        c[u] = 0;
-        sj[u] = 0.0f;
-        if (p < total && o < n_use) {
-          c[u] = CB[(j0 + ch) * K + sO[o]];
-          sj[u] = SCB[j0 + ch];
+      for (int g = 0; g < kGather; ++g) {
+        rg[g] = rr;
+        ug[g] = uu;
+        if (++uu == nu) {
+          uu = 0;
+          ++rr;
         }
       }
+      r0 = rr;
+      u0 = uu;
+      int8_t c[kGather];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t p = p0 + u * 256 + tid;
-        const uint32_t ch = p / np, o = p - ch * np;
-        if (p < total) Wo[(j0 + ch) * ldo + o] = dequant_weight(c[u], sj[u]);
+      for (int g = 0; g < kGather; ++g) {
+        const int64_t o = ug[g] * 64 + lane;
+        c[g] = (q0 + g < items && o < n_use) ? CB[(j0 + wave + 4 * rg[g]) * K + sO[o]]
+                                             : (int8_t)0;
+      }
+#pragma unroll
+      for (int g = 0; g < kGather; ++g) {
+        const int64_t o = ug[g] * 64 + lane;
+        if (q0 + g < items && o < n_pad) {
+          const int64_t j = j0 + wave + 4 * rg[g];
+          Wo[j * ldo + o] = dequant_weight(c[g], SCB[j]);
+        }
       }
     }
   } else {
@@ -411,6 +466,7 @@ __global__ __launch_bounds__(256) void k_prep(
       for (int64_t o = n_use + lane; o < n_pad; o += 64) worow[o] = (_Float16)0.0f;
     }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 size_t prep_lds_bytes(int64_t K, int64_t ocap) {
@@ -419,7 +475,7 @@ size_t prep_lds_bytes(int64_t K, int64_t ocap) {
 }
 
 void launch_prep(const PrepArgs& p, hipStream_t st) {
-  const int64_t nrowblk = p.Xq ? p.T : 0;
+  const int64_t nrowblk = p.Xq ? ceil_div(p.T, kRowsPerPrepBlock) : 0;
   const int64_t nwoblk = p.Wo ? ceil_div(p.N, kChansPerWoBlock) : 0;
   const size_t lds = prep_lds_bytes(p.K, p.ocap);
   dim3 g((unsigned)(nrowblk + nwoblk > 0 ? nrowblk + nwoblk : 1));
@@ -431,9 +487,9 @@ void launch_prep(const PrepArgs& p, hipStream_t st) {
                                     p.ocap);
   };
   if (p.vec)
-    go(k_prep<true>);
+    go(k_prep<true, kRowsPerPrepBlock>);
   else
-    go(k_prep<false>);
+    go(k_prep<false, kRowsPerPrepBlock>);
 }
 
 // Y[i, j] = bias[j] (or 0): the layer with K == 0 (no columns, no outliers).

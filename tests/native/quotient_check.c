@@ -12,6 +12,13 @@
  * differ.  It also walks every product p = fl32(c * s) of a code c in
  * [-127, 127] and an fp16 scale s (the dequantized outlier weights) and
  * checks the same construction for p / 127 against fl32(p / 127).
+ *
+ * The kernels round q to the nearest integer, half away from zero, as
+ * (int)(fl32(q + copysign(0.5, q))) (truncating conversion).  That is not
+ * round-half-away-from-zero for every float (q + 0.5 can itself round up,
+ * e.g. for q just below 0.5), so it is also checked here against the exact
+ * rule on every quotient the pairs above produce.  A zero scale uses r = 0,
+ * which must give code 0 for x = 0 (the only x a zero absmax allows).
  * Exit status 0 iff every count is zero.
  */
 #include <math.h>
@@ -42,8 +49,15 @@ static float half_to_float(uint16_t h) {
 
 static double rhaz(float v) { return trunc((double)v + copysign(0.5, (double)v)); }
 
+/* the kernels' rounding: fp32 add of +-0.5, then a truncating conversion */
+static int gpu_round(float q) {
+  const volatile float h = copysignf(0.5f, q);
+  const volatile float t = q + h;
+  return (int)t;
+}
+
 int main(void) {
-  long pairs = 0, quot_mismatch = 0, code_mismatch = 0;
+  long pairs = 0, quot_mismatch = 0, code_mismatch = 0, round_mismatch = 0;
   for (uint32_t hs = 1; hs < 0x7c00; ++hs) {       /* every positive finite s */
     const volatile float s = half_to_float((uint16_t)hs);
     const float r = 1.0f / s;
@@ -57,7 +71,13 @@ int main(void) {
       ++pairs;
       if (q != ref) ++quot_mismatch;
       if (rhaz(q) != rhaz(ref)) ++code_mismatch;
+      if ((double)gpu_round(q) != rhaz(ref) || gpu_round(-q) != -gpu_round(q)) ++round_mismatch;
     }
+  }
+  {  /* zero scale: r = 0 */
+    const volatile float s = 0.0f, r = 0.0f, n = 0.0f * 127.0f;
+    const float q0 = n * r, e = fmaf(-q0, s, n), q = fmaf(e, r, q0);
+    if (gpu_round(q) != 0) ++round_mismatch;
   }
   long deq = 0, deq_mismatch = 0;
   const volatile float d127 = 127.0f;
@@ -74,7 +94,9 @@ int main(void) {
       if (q != ref) ++deq_mismatch;
     }
   }
-  printf("pairs %ld quotient_mismatch %ld code_mismatch %ld dequant %ld dequant_mismatch %ld\n",
-         pairs, quot_mismatch, code_mismatch, deq, deq_mismatch);
-  return (quot_mismatch == 0 && code_mismatch == 0 && deq_mismatch == 0) ? 0 : 1;
+  printf("pairs %ld quotient_mismatch %ld code_mismatch %ld round_mismatch %ld dequant %ld "
+         "dequant_mismatch %ld\n",
+         pairs, quot_mismatch, code_mismatch, round_mismatch, deq, deq_mismatch);
+  return (quot_mismatch == 0 && code_mismatch == 0 && round_mismatch == 0 && deq_mismatch == 0)
+             ? 0 : 1;
 }

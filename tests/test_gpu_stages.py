@@ -64,9 +64,17 @@ def _detect_cases():
     yield d["X"], 1e-6                              # every non-zero column
     d = make_random_case(61, 2048, 512, 8, x_sigma=1.5)
     yield d["X"], 6.0                               # many natural outliers
+    d = make_random_case(63, 24, 20000, 8, n_planted=9)
+    X = d["X"].copy()
+    X[5, 19999] = 7.0                               # outliers in mask words past 512
+    X[7, 16400] = -9.0
+    yield X, 6.0
 
 
-@pytest.mark.parametrize("case", list(range(len(SHAPES) + 4)))
+N_DETECT_CASES = len(SHAPES) + 5
+
+
+@pytest.mark.parametrize("case", list(range(N_DETECT_CASES)))
 def test_find_outliers_bitexact(i8, case):
     X, thr = list(_detect_cases())[case]
     T, K = X.shape
@@ -101,7 +109,7 @@ def _mask_of(Oo, K):
     return m.view(np.int32)
 
 
-@pytest.mark.parametrize("case", list(range(len(SHAPES) + 4)))
+@pytest.mark.parametrize("case", list(range(N_DETECT_CASES)))
 def test_quantize_rows_bitexact(i8, case):
     X, thr = list(_detect_cases())[case]
     T, K = X.shape
