@@ -99,7 +99,7 @@ def main() -> int:
                     help="rotate this many copies of X/CB/SCB/Y so the 256 MB last-level "
                          "cache cannot hold one step's inputs from the step before")
     ap.add_argument("--cpu-cols", type=int, default=20480)
-    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--cpu-reps", type=int, default=15)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16", action="store_true")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
