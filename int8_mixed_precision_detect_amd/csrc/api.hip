@@ -159,8 +159,6 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   pa.Wo = Wo;
   pa.ocap = max_outliers < kOcap ? max_outliers : kOcap;
   pa.vec = xvec;
-  launch_prep(pa, stream);
-  if (ev) (void)hipEventRecord(ev[2], stream);
 
   GemmArgs a{};
   a.A = CB;
@@ -176,11 +174,20 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   a.Xo = Xo;
   a.ldo = L.ldo;
   a.counts = counts;
+  a.O = O;
   a.max_o = max_outliers;
   a.bias = (const _Float16*)bias;
   a.Y = (_Float16*)Y;
-  const hipError_t ge = gemm_i8_supported(a) ? launch_gemm_i8_fused(a, stream)
-                                             : launch_gemm_fused(a, stream);
+  // few tokens: the streaming kernel, which extracts small outlier weight
+  // sets itself; otherwise the tiled kernel (or the generic one)
+  const bool few = gemv_i8_supported(a);
+  pa.wo_skip = few ? kGemvOcap : -1;
+  launch_prep(pa, stream);
+  if (ev) (void)hipEventRecord(ev[2], stream);
+
+  const hipError_t ge = few                    ? launch_gemv_i8_fused(a, stream)
+                        : gemm_i8_supported(a) ? launch_gemm_i8_fused(a, stream)
+                                               : launch_gemm_fused(a, stream);
   if (ge != hipSuccess) return I8MM_ERR_HIP;
   if (ev) (void)hipEventRecord(ev[3], stream);
   return hip_status();
@@ -235,6 +242,7 @@ i8mm_status int8_quantize_rows(const void* X, int64_t T, int64_t K, const uint32
   pa.Xo = (_Float16*)Xo;
   pa.ldo = ldo;
   pa.ocap = max_outliers < kOcap ? max_outliers : kOcap;
+  pa.wo_skip = -1;
   pa.vec = (K % 8 == 0) && aligned(X, 16);
   launch_prep(pa, stream);
   return hip_status();
@@ -259,6 +267,7 @@ i8mm_status int8_outlier_weights(const int8_t* CB, const float* SCB, int64_t N, 
   pa.Wo = (_Float16*)Wo;
   pa.ldo = ldo;
   pa.ocap = max_outliers < kOcap ? max_outliers : kOcap;
+  pa.wo_skip = -1;
   pa.vec = false;
   launch_prep(pa, stream);
   return hip_status();
@@ -280,8 +289,9 @@ i8mm_status int8_gemm_s32(const int8_t* A, int64_t lda, const int8_t* B, int64_t
   a.T = T;
   a.K = K;
   a.C = C;
-  const hipError_t ge = gemm_i8_supported(a) ? launch_gemm_i8_s32(a, stream)
-                                             : launch_gemm_s32(a, stream);
+  const hipError_t ge = gemv_i8_supported(a)   ? launch_gemv_i8_s32(a, stream)
+                        : gemm_i8_supported(a) ? launch_gemm_i8_s32(a, stream)
+                                               : launch_gemm_s32(a, stream);
   if (ge != hipSuccess) return I8MM_ERR_HIP;
   return hip_status();
 }

@@ -358,24 +358,12 @@ int cu_count() {
 // waves, and B 512 tiles, 2 full waves.
 template <int MODE>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
-#ifdef I8MM_CFG
-#if I8MM_CFG == 20
-  return launch_cfg<256, 256, 64, 128, 2, 128, MODE>(a, st);
-#elif I8MM_CFG == 25
-  return launch_cfg<320, 256, 80, 128, 2, 128, MODE>(a, st);
-#elif I8MM_CFG == 26
-  return launch_cfg<320, 256, 160, 64, 2, 128, MODE>(a, st);
-#else
-#error "unknown I8MM_CFG"
-#endif
-#else
   const int64_t cus = cu_count();
   auto cost = [&](int64_t bm, int64_t bn) {
     return ceil_div(ceil_div(a.N, bm) * ceil_div(a.T, bn), cus) * bm * bn;
   };
   if (cost(320, 256) < cost(256, 256)) return launch_cfg<320, 256, 80, 128, 2, 128, MODE>(a, st);
   return launch_cfg<256, 256, 64, 128, 2, 128, MODE>(a, st);
-#endif
 }
 }  // namespace
 

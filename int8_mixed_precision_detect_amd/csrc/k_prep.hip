@@ -219,7 +219,9 @@ void launch_compact(const uint32_t* mask, int64_t K, int32_t* O, int32_t* counts
 //     row: masked absmax -> sx, codes -> Xq (0 on outlier and pad columns),
 //     X[:, O] -> Xo (0 on pad columns);
 //   workgroups [R, R + ceil(N/16)): 16 output channels each:
-//     Wo[j, o] = fp16(fl32(fl32(CB[j, O[o]] * SCB[j]) / 127)), 0 on pad.
+//     Wo[j, o] = fp16(fl32(fl32(CB[j, O[o]] * SCB[j]) / 127)), 0 on pad
+//     (skipped for outlier sets of at most wo_skip columns, which the
+//     few-token product kernel extracts itself).
 // A row workgroup issues its loads of X before rebuilding the outlier set
 // (they do not depend on it), so the two latencies overlap.  O is
 // ascending, so the gathers of consecutive o by consecutive lanes read
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(256) void k_prep(
     int32_t* __restrict__ O_out, int32_t* __restrict__ counts, int64_t max_o,
     int8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sx, _Float16* __restrict__ Xo,
     int64_t ldo, int64_t nrowblk, const int8_t* __restrict__ CB, const float* __restrict__ SCB,
-    int64_t N, _Float16* __restrict__ Wo, int64_t ocap) {
+    int64_t N, _Float16* __restrict__ Wo, int64_t ocap, int64_t wo_skip) {
   // The body uses amdgcn-only types (buffer resources); the host pass only
   // needs the kernel's signature to emit its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(256) void k_prep(
   // ---- dequantized outlier weight rows, 16 channels
   const int64_t j0 = ((int64_t)blockIdx.x - nrowblk) * kChansPerWoBlock;
   const int64_t nch = min((int64_t)kChansPerWoBlock, N - j0);
-  if (n_pad == 0 || nch <= 0) return;
+  if (n_pad == 0 || nch <= 0 || n_use <= wo_skip) return;
   if (listed) {
     // per wave: items (channel r, chunk u of 64 outputs), wave-uniform, so
     // the channel's row address and scale stay scalar; a lane gathers
@@ -484,7 +486,7 @@ void launch_prep(const PrepArgs& p, hipStream_t st) {
                               (int)lds);
     kern<<<g, dim3(256), lds, st>>>(p.X, p.T, p.K, p.mask, p.O_out, p.counts, p.max_o, p.Xq,
                                     p.ldq, p.sx, p.Xo, p.ldo, nrowblk, p.CB, p.SCB, p.N, p.Wo,
-                                    p.ocap);
+                                    p.ocap, p.wo_skip);
   };
   if (p.vec)
     go(k_prep<true, kRowsPerPrepBlock>);

@@ -36,8 +36,9 @@ struct PrepArgs {
   const float* SCB;
   int64_t N;
   _Float16* Wo;
-  int64_t ocap;  // outlier-list capacity in LDS (entries)
-  bool vec;      // 16-byte aligned rows of X (K % 8 == 0)
+  int64_t ocap;     // outlier-list capacity in LDS (entries)
+  int64_t wo_skip;  // Wo is built only when the outlier set exceeds this
+  bool vec;         // 16-byte aligned rows of X (K % 8 == 0)
 };
 size_t prep_lds_bytes(int64_t K, int64_t ocap);
 void launch_prep(const PrepArgs& p, hipStream_t st);
@@ -58,6 +59,7 @@ struct GemmArgs {
   const _Float16* Xo;
   int64_t ldo;
   const int32_t* counts;
+  const int32_t* O;  // ascending outlier list (the few-token kernel)
   int64_t max_o;
   const _Float16* bias;
   _Float16* Y;
@@ -74,5 +76,14 @@ hipError_t launch_gemm_s32(const GemmArgs& a, hipStream_t st);
 bool gemm_i8_supported(const GemmArgs& a);
 hipError_t launch_gemm_i8_fused(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_i8_s32(const GemmArgs& a, hipStream_t st);
+
+// Few tokens (1 <= T <= kGemvMaxT), 16-byte aligned operands: a kernel that
+// streams CB once.  It extracts the outlier weights itself for outlier sets
+// of at most kGemvOcap columns (the step-2 kernel then skips Wo).
+constexpr int64_t kGemvMaxT = 32;
+constexpr int64_t kGemvOcap = 128;
+bool gemv_i8_supported(const GemmArgs& a);
+hipError_t launch_gemv_i8_fused(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemv_i8_s32(const GemmArgs& a, hipStream_t st);
 
 }  // namespace i8mm

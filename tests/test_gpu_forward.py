@@ -125,6 +125,27 @@ def test_wide_channel_tile(i8):
     _full_check(i8, d["X"], d["W"], d["bias"], 6.0, "320-channel tiles 2048x256x20380")
 
 
+@pytest.mark.parametrize("T,K,N,planted", [(1, 1040, 70, 3), (5, 1040, 70, 40), (32, 2048, 1000, 6),
+                                            (17, 12288, 300, 12)])
+def test_few_tokens(i8, T, K, N, planted):
+    # T <= 32 runs the streaming product kernel, which picks the outlier
+    # weights out of the CB bytes it streams; an outlier in the last, partial
+    # 64-byte k-step exercises the K tail
+    d = make_random_case(T * 11 + K + N, T, K, N, n_planted=planted, bias=True)
+    X = d["X"].copy()
+    X[0, K - 1] = 9.0
+    _full_check(i8, X, d["W"], d["bias"], 6.0, f"few tokens {T}x{K}x{N}")
+
+
+def test_few_tokens_wide_outlier_set(i8):
+    # more outlier columns than the streaming kernel extracts itself (128):
+    # it takes Wo from the workspace, built by the step-2 kernel
+    d = make_random_case(907, 16, 2048, 300, n_planted=0, bias=True)
+    n = len(O.find_outliers(d["X"], 2.5))
+    assert n > 128
+    _full_check(i8, d["X"], d["W"], d["bias"], 2.5, "few tokens, wide set")
+
+
 @pytest.mark.parametrize("T,K,N,thr", [(64, 2048, 200, 3.0), (48, 8192, 96, 2.0)])
 def test_wide_outlier_sets(i8, T, K, N, thr):
     # ~16% and ~89% of the columns are outliers; the second set is larger
