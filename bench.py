@@ -29,9 +29,10 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 GEMM_SOURCES = ["int8_mixed_precision_detect_amd/csrc/k_gemm_i8.hip",
+                "int8_mixed_precision_detect_amd/csrc/k_gemv.hip",
                 "int8_mixed_precision_detect_amd/csrc/common.h",
                 "int8_mixed_precision_detect_amd/csrc/kernels.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_13b_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_{}_traffic.txt")  # per workload
 
 
 def kernel_fingerprint() -> str:
@@ -45,10 +46,11 @@ def kernel_fingerprint() -> str:
 def read_traffic(workload: str):
     """HBM bytes per launch of the product kernel from the committed counter
     summary, or None when it is missing or was taken on other kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILE.format(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, _, v = line.partition(":")
@@ -175,16 +177,30 @@ def main() -> int:
     ops = 2.0 * T * N * K
     tops = ops / (ms_per_step * 1e-3) / 1e12
     gemm_ms = stage_avg[2]
-    achieved = ops / (gemm_ms * 1e-3) / 1e12
     traffic = read_traffic(args.workload)
     n_pad = -(-n_o // 32) * 32
+    ldq = -(-K // 64) * 64
+    if T <= 32:
+        # few tokens: the product streams CB once -- an HBM-bound kernel;
+        # algorithmic bytes per launch: CB, Xq, Xo, Y (and the outlier CB
+        # bytes it picks from the same stream)
+        gemm_bytes = N * K + T * ldq + 2 * T * n_pad + 2 * T * N
+        achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "kernel": "k_gemv_i8 (few-token int8 product + epilogue)",
+                    "avg_ms": round(gemm_ms, 5), "algorithmic_bytes_per_launch": gemm_bytes}
+    else:
+        achieved = ops / (gemm_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                    "traffic": traffic, "kernel": "k_gemm_i8 (fused int8 product + epilogue)",
+                    "avg_ms": round(gemm_ms, 5), "algorithmic_ops_per_launch": ops}
     detect_bytes = 2.0 * T * K
     # step-2 prep: read X, write Xq (ldq = K rounded to 64), sx and Xo; the
-    # outlier weights Wo (gather of CB[:, O], fp16 write) are built here only
-    # for sets above 96 columns, else inside the product kernel
-    ldq = -(-K // 64) * 64
+    # outlier weights Wo (gather of CB[:, O], fp16 write) when it builds them
     quant_bytes = 2.0 * T * K + T * ldq + 4 * T + 2 * T * n_pad
-    if n_o > 96:
+    if T > 32 or n_o > 128:
         quant_bytes += N * n_o + 2 * N * n_pad
 
     result = {
@@ -203,10 +219,7 @@ def main() -> int:
         "config": {"workload": f"{args.workload}-scale first FF layer (LLM.int8() linear)",
                    "T": T, "K": K, "N": N, "threshold": wl.threshold, "n_outliers": n_o,
                    "bias": d["bias"] is not None, "buffer_copies": copies},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                     "traffic": traffic, "kernel": "k_gemm (fused int8 product + epilogue)",
-                     "avg_ms": round(gemm_ms, 5), "algorithmic_ops_per_launch": ops},
+        "roofline": roofline,
         "stages_ms": {"detect": round(stage_avg[0], 5), "quantize_gather": round(stage_avg[1], 5),
                       "product": round(stage_avg[2], 5), "whole_call": round(stage_avg[3], 5)},
         "stages_hbm_frac": {
