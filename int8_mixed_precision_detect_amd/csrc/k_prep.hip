@@ -231,6 +231,7 @@ void launch_compact(const uint32_t* mask, int64_t K, int32_t* O, int32_t* counts
 // ---------------------------------------------------------------------------
 constexpr int kChansPerWoBlock = 16;
 constexpr int kMaskWords = 2;  // mask words a thread requests before the row
+constexpr int kRowChunks = 4;  // 16-byte chunks of a CB row a thread streams (K <= 16384)
 // One row per workgroup measured best across the first-FF shapes (2 and 4
 // rows per workgroup: 13B-scale 12.2 / 10.9 us against 11.8 us, 175B-scale
 // 51 / 60 us against 46 us, 32-token decode 10 / 16 us against 7 us).
@@ -300,7 +301,12 @@ __global__ __launch_bounds__(256) void k_prep(
   const int64_t n_use = (int64_t)n_o < max_o ? n_o : max_o;
   const int64_t n_pad = round_up(n_use, 32);
   const bool listed = n_use <= ocap;
-  if (listed) outlier_list<256>(smask, spref, KW, n_use, sO);
+  // Wide outlier sets touch nearly every cache line of a CB row: the channel
+  // workgroups then stream whole rows (through the LDS that would hold O)
+  // instead of gathering -- see below.
+  const bool wo_stream = !row_block && n_use * 64 >= K && K % 16 == 0 && K + 16 <= ocap * 4 &&
+                         K <= 256 * kRowChunks * 16 && (((uintptr_t)CB) & 15) == 0;
+  if (listed && !wo_stream) outlier_list<256>(smask, spref, KW, n_use, sO);
   if (blockIdx.x == 0 && counts) {
     outlier_list<256>(smask, spref, KW, max_o, O_out);
     if (tid == 0) {
@@ -409,7 +415,46 @@ __global__ __launch_bounds__(256) void k_prep(
   const int64_t j0 = ((int64_t)blockIdx.x - nrowblk) * kChansPerWoBlock;
   const int64_t nch = min((int64_t)kChansPerWoBlock, N - j0);
   if (n_pad == 0 || nch <= 0 || n_use <= wo_skip) return;
-  if (listed) {
+  if (wo_stream) {
+    // Rows streamed whole: row r's 16-byte chunks go to LDS (coalesced
+    // loads), the next row's loads are in flight while this one's outlier
+    // bytes are picked by walking the mask words (output position from the
+    // prefix scan) and dequantized.
+    char* srow = (char*)sm + round_up((2 * KW + 1) * 4, 16);
+    const int64_t nck = K / 16;
+    v4i nx[kRowChunks];
+    auto load_row = [&](int64_t j) {
+#pragma unroll
+      for (int u = 0; u < kRowChunks; ++u) {
+        const int64_t c = tid + 256 * u;
+        nx[u] = c < nck ? *(const v4i*)(CB + j * K + 16 * c) : v4i{0, 0, 0, 0};
+      }
+    };
+    load_row(j0);
+    for (int64_t r = 0; r < nch; ++r) {
+      const int64_t j = j0 + r;
+#pragma unroll
+      for (int u = 0; u < kRowChunks; ++u) {
+        const int64_t c = tid + 256 * u;
+        if (c < nck) *(v4i*)(srow + 16 * c) = nx[u];
+      }
+      __syncthreads();
+      if (r + 1 < nch) load_row(j + 1);
+      const float sj = SCB[j];
+      _Float16* worow = Wo + j * ldo;
+      for (int64_t w = tid; w < KW; w += 256) {
+        uint32_t mb = smask[w];
+        int64_t o = spref[w];
+        while (mb && o < n_use) {
+          const int b = __ffs(mb) - 1;
+          mb &= mb - 1;
+          worow[o++] = dequant_weight(srow[w * 32 + b], sj);
+        }
+      }
+      for (int64_t o = n_use + tid; o < n_pad; o += 256) worow[o] = (_Float16)0.0f;
+      __syncthreads();  // the row buffer is rewritten next
+    }
+  } else if (listed) {
     // per wave: items (channel r, chunk u of 64 outputs), wave-uniform, so
     // the channel's row address and scale stay scalar; a lane gathers
     // output o = 64u + lane; kGather items in flight
