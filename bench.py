@@ -29,7 +29,6 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 GEMM_SOURCES = ["int8_mixed_precision_detect_amd/csrc/k_gemm_i8.hip",
-                "int8_mixed_precision_detect_amd/csrc/k_gemv.hip",
                 "int8_mixed_precision_detect_amd/csrc/common.h",
                 "int8_mixed_precision_detect_amd/csrc/kernels.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_{}_traffic.txt")  # per workload
@@ -188,7 +187,7 @@ def main() -> int:
         achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                    "kernel": "k_gemv_i8 (few-token int8 product + epilogue)",
+                    "kernel": "k_gemm_i8, few-token tiles (int8 product + epilogue)",
                     "avg_ms": round(gemm_ms, 5), "algorithmic_bytes_per_launch": gemm_bytes}
     else:
         achieved = ops / (gemm_ms * 1e-3) / 1e12

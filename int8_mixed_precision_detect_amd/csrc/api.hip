@@ -178,16 +178,14 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   a.max_o = max_outliers;
   a.bias = (const _Float16*)bias;
   a.Y = (_Float16*)Y;
-  // few tokens: the streaming kernel, which extracts small outlier weight
-  // sets itself; otherwise the tiled kernel (or the generic one)
-  const bool few = gemv_i8_supported(a);
-  pa.wo_skip = few ? kGemvOcap : -1;
+  // aligned operands: the tiled kernel (for few tokens it extracts small
+  // outlier weight sets itself); otherwise the generic one
+  const bool fast = gemm_i8_supported(a);
+  pa.wo_skip = fast && T <= kFewT ? kFewOcap : -1;
   launch_prep(pa, stream);
   if (ev) (void)hipEventRecord(ev[2], stream);
 
-  const hipError_t ge = few                    ? launch_gemv_i8_fused(a, stream)
-                        : gemm_i8_supported(a) ? launch_gemm_i8_fused(a, stream)
-                                               : launch_gemm_fused(a, stream);
+  const hipError_t ge = fast ? launch_gemm_i8_fused(a, stream) : launch_gemm_fused(a, stream);
   if (ge != hipSuccess) return I8MM_ERR_HIP;
   if (ev) (void)hipEventRecord(ev[3], stream);
   return hip_status();
@@ -289,9 +287,8 @@ i8mm_status int8_gemm_s32(const int8_t* A, int64_t lda, const int8_t* B, int64_t
   a.T = T;
   a.K = K;
   a.C = C;
-  const hipError_t ge = gemv_i8_supported(a)   ? launch_gemv_i8_s32(a, stream)
-                        : gemm_i8_supported(a) ? launch_gemm_i8_s32(a, stream)
-                                               : launch_gemm_s32(a, stream);
+  const hipError_t ge = gemm_i8_supported(a) ? launch_gemm_i8_s32(a, stream)
+                                             : launch_gemm_s32(a, stream);
   if (ge != hipSuccess) return I8MM_ERR_HIP;
   return hip_status();
 }

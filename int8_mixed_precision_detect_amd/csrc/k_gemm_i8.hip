@@ -43,7 +43,13 @@ namespace i8mm {
 
 namespace {
 
-constexpr int MODE_I32 = 0, MODE_FUSED = 1;
+// MODE_FUSED_X: the fused product for few tokens (one token tile, one wave
+// owning every channel row of its tile), which also extracts the outlier
+// weights itself -- see the int8 loop.
+constexpr int MODE_I32 = 0, MODE_FUSED = 1, MODE_FUSED_X = 2;
+// LDS beyond the slices for MODE_FUSED_X: the outlier list and the tile's
+// X[:, O] values ([kFewOcap][BN] halves)
+constexpr size_t few_lds(int BN) { return (size_t)kFewOcap * 4 + (size_t)kFewOcap * BN * 2; }
 using I8Slices = std::false_type;
 using F16Slices = std::true_type;
 
@@ -57,10 +63,14 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// wait until at most n*PW of this wave's loads are outstanding (n < 4)
+// wait until at most n*PW of this wave's loads are outstanding
 template <int PW>
 __device__ __forceinline__ void wait_slices(int n) {
-  if (n >= 3)
+  if (n >= 5)
+    wait_vm<5 * PW < 64 ? 5 * PW : 63>();
+  else if (n == 4)
+    wait_vm<4 * PW < 64 ? 4 * PW : 63>();
+  else if (n == 3)
     wait_vm<3 * PW < 64 ? 3 * PW : 63>();
   else if (n == 2)
     wait_vm<2 * PW>();
@@ -75,7 +85,9 @@ __device__ __forceinline__ void wait_lgkm0() {
 
 }  // namespace
 
-template <int BM, int BN, int WM, int WN, int S, int KB, int MODE>
+// NTA: the weight operand's slice loads are non-temporal (streamed once: the
+// few-token shapes, where each weight byte is used by one workgroup)
+template <int BM, int BN, int WM, int WN, int S, int KB, int MODE, bool NTA>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs a) {
   // The body uses amdgcn-only types (buffer resources); the host pass only
   // needs the kernel's signature to emit its launch stub.
@@ -89,7 +101,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   constexpr int PW = (ACH + BCH) / NWAVE;        // ... per wave
   constexpr int KS = KB / 64;                    // MFMA k-steps per slice
   static_assert(KB == 64 || KB == 128, "slice width");
-  static_assert(S >= 2 && S <= 4 && (S - 1) * PW < 64, "slices in flight");
+  static_assert(S >= 2 && S <= 6 && (S - 1) * PW < 64, "slices in flight");
+  static_assert(MODE != MODE_FUSED_X || (NWAVE == 1 && BM <= 64), "one wave, one lane a row");
   static_assert((ACH + BCH) % NWAVE == 0, "slice pieces must split evenly over waves");
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -108,7 +121,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   // resource (base in SGPRs), a lane's 32-bit offset (row * ld + its chunk)
   // is fixed for the whole K loop and the K position goes in the scalar
   // offset, so a load costs no per-lane address arithmetic.
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wv = NWAVE == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave);
   __amdgpu_buffer_rsrc_t rsA, rsB;
   uint32_t voff[PW];
   // a lane's chunk within its row: rows of a piece start at multiples of
@@ -138,19 +151,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     const int off = (j < ACH) ? j * 1024 : BM * KB + (j - ACH) * 1024;
     return (__attribute__((address_space(3))) void*)(lds + buf * STAGE + off);
   };
+  // one 1 KB piece; the cache policy is an immediate, hence the two calls
+  // (the A/B choice is wave-uniform)
+  auto dma = [&](int u, void* dst, uint32_t vo, int64_t k0) {
+    auto d = (__attribute__((address_space(3))) void*)dst;
+    if (wv * PW + u < ACH)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, d, 16, vo, (int)k0, 0, NTA ? 2 : 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, d, 16, vo, (int)k0, 0, 0);
+  };
   auto issue = [&](int buf, int64_t k0, int64_t Kb) {
     if (k0 + KB <= Kb) {
 #pragma unroll
-      for (int u = 0; u < PW; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wv * PW + u < ACH ? rsA : rsB, lds_dst(buf, u), 16,
-                                                 voff[u], (int)k0, 0, 0);
+      for (int u = 0; u < PW; ++u) dma(u, (void*)lds_dst(buf, u), voff[u], k0);
     } else {
 #pragma unroll
-      for (int u = 0; u < PW; ++u) {
-        const uint32_t vo = (k0 + kc < Kb) ? voff[u] : 0x80000000u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wv * PW + u < ACH ? rsA : rsB, lds_dst(buf, u), 16,
-                                                 vo, (int)k0, 0, 0);
-      }
+      for (int u = 0; u < PW; ++u)
+        dma(u, (void*)lds_dst(buf, u), (k0 + kc < Kb) ? voff[u] : 0x80000000u, k0);
     }
   };
   // fragment of 16 rows at k-step h of a slice: lane -> row (lane & 15),
@@ -218,14 +235,117 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     }
   };
 
+  // Few tokens (MODE_FUSED_X): the outlier weights come out of the CB bytes
+  // this workgroup stages anyway.  O is ascending, so one pointer follows the
+  // k walk: when slice kt holds the next outlier column, the lane owning each
+  // channel row reads that byte from LDS, dequantizes it and adds its
+  // products with the tile's X[:, O] values (staged in LDS) to px, one fp32
+  // sum per token.  The lane also shifts the value into wb, a window of the
+  // last 64 columns of its Wo row held in registers, which goes to the
+  // workspace after the K loop (and every 64th column for wider sets).  The
+  // K loop loads and stores nothing in global memory but the slices: a store
+  // there, waited for with the slices, costs about a slice's time.
+  int64_t n_use = 0;
+  bool inloop = false;
+  int64_t nxt = 0;
+  int nextc = 0x7fffffff;
+  float sjx = 0.0f;
+  constexpr int PX = MODE == MODE_FUSED_X ? BN : 1;  // (nothing of this in other modes)
+  float px[PX];
+#pragma unroll
+  for (int t = 0; t < PX; ++t) px[t] = 0.0f;
+  int32_t* sO = (int32_t*)(lds + S * STAGE);                                   // [kFewOcap]
+  _Float16* sXo = (_Float16*)(lds + S * STAGE + kFewOcap * 4);                 // [kFewOcap][BN]
+  constexpr int WB = MODE == MODE_FUSED_X ? 32 : 1;  // dwords of the window
+  uint32_t wb[WB];
+#pragma unroll
+  for (int q = 0; q < WB; ++q) wb[q] = 0u;
+  // window shifts down by one half, h comes in at the top
+  auto wb_push = [&](uint32_t h) {
+#pragma unroll
+    for (int q = 0; q < WB; ++q)
+      wb[q] = __builtin_amdgcn_alignbit(q + 1 < WB ? wb[q + 1] : h, wb[q], 16);
+  };
+  // ... by d halves (uniform, 0 <= d < 2 * WB), zeros in at the top
+  auto wb_shift = [&](int d) {
+    if (d & 1) {
+#pragma unroll
+      for (int q = 0; q < WB; ++q)
+        wb[q] = __builtin_amdgcn_alignbit(q + 1 < WB ? wb[q + 1] : 0u, wb[q], 16);
+    }
+#pragma unroll
+    for (int b = 1; (1 << b) < 2 * WB; ++b) {
+      if (d & (1 << b)) {
+        const int w = 1 << (b - 1);  // dwords
+#pragma unroll
+        for (int q = 0; q < WB; ++q) wb[q] = q + w < WB ? wb[q + w] : 0u;
+      }
+    }
+  };
+  // the window holds Wo columns o0 .. o0 + 2 WB - 1 of this lane's row; the
+  // 8-column pieces below lim go out
+  auto wb_store = [&](int64_t o0, int64_t lim) {
+    if (m0 + lane < a.N) {
+      _Float16* dst = (_Float16*)a.Wo + (m0 + lane) * a.ldo + o0;
+#pragma unroll
+      for (int q = 0; q < WB / 4; ++q)
+        if (o0 + 8 * q < lim) *(v4u*)(dst + 8 * q) = v4u{wb[4 * q], wb[4 * q + 1], wb[4 * q + 2], wb[4 * q + 3]};
+    }
+  };
+  // run while the first slices are in flight
+  auto few_setup = [&]() {
+    if constexpr (MODE == MODE_FUSED_X) {
+      const int64_t n_o = a.counts[0];
+      n_use = n_o < a.max_o ? n_o : a.max_o;
+      inloop = n_use <= kFewOcap;
+      if (inloop) {
+        for (int64_t o = lane; o < n_use; o += 64) {
+          sO[o] = a.O[o];
+          // unconditional loads (rows clamped), so that they are all in flight at once
+          _Float16 xv[BN];
+#pragma unroll
+          for (int t = 0; t < BN; ++t) {
+            const int64_t tt = n0 + t < a.T ? n0 + t : a.T - 1;
+            xv[t] = a.Xo[tt * a.ldo + o];
+          }
+#pragma unroll
+          for (int t = 0; t < BN; ++t) sXo[o * BN + t] = n0 + t < a.T ? xv[t] : (_Float16)0.0f;
+        }
+      }
+      if (lane < BM && m0 + lane < a.N) sjx = a.SCB[m0 + lane];
+      asm volatile("" ::"v"(sjx));  // waited for here rather than inside the K loop
+      __syncthreads();
+      if (inloop && n_use > 0) nextc = __builtin_amdgcn_readfirstlane(sO[0]);
+    }
+  };
+  auto extract = [&](int buf, int64_t kbase) {
+    while (nextc < kbase + KB) {
+      const int off = nextc - (int)kbase;  // 0 .. KB-1
+      if (lane < BM) {
+        const int chunk = (off >> 4) ^ swz<KB>(lane);
+        const int c = (int8_t)lds[buf * STAGE + lane * KB + chunk * 16 + (off & 15)];
+        const _Float16 wo = dequant_weight(c, sjx);
+        wb_push(__builtin_bit_cast(uint16_t, wo));
+        if ((nxt & 63) == 63) wb_store(nxt - 63, n_use);
+        const float wf = (float)wo;
+        const _Float16* xr = sXo + nxt * BN;
+#pragma unroll
+        for (int t = 0; t < PX; ++t) px[t] += (float)xr[t] * wf;
+      }
+      ++nxt;
+      nextc = nxt < n_use ? __builtin_amdgcn_readfirstlane(sO[nxt]) : 0x7fffffff;
+    }
+  };
+
   // K loop over Kb bytes of the operands set up last: S slices in flight,
   // one barrier per slice.  LDS must be free of earlier readers on entry.
-  auto run = [&](auto f16, int64_t Kb) {
+  // primed() runs once the first slices are issued.
+  auto run = [&](auto f16, int64_t Kb, auto&& primed) {
     const int64_t nk = ceil_div(Kb, KB);
-    if (nk <= 0) return;
 #pragma unroll
     for (int s = 0; s < S; ++s)
       if (s < nk) issue(s, s * KB, Kb);
+    primed();
     for (int64_t kt = 0; kt < nk; ++kt) {
       // Slice kt must have landed.  Issued so far: slices up to
       // min(kt + S - 2, nk - 1) (up to S - 1 before the loop); the ones
@@ -237,6 +357,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       // done with slice kt-1, whose buffer is refilled with slice kt-1+S
       __builtin_amdgcn_s_barrier();
       if (kt >= 1 && kt - 1 + S < nk) issue((int)((kt - 1) % S), (kt - 1 + S) * KB, Kb);
+      if constexpr (MODE == MODE_FUSED_X && !decltype(f16)::value) extract((int)(kt % S), kt * KB);
       compute(f16, (int)(kt % S));
       // keeps the epilogue's loads (scales, bias) below the loop instead of
       // hoisted above it, where they would hold registers throughout
@@ -245,7 +366,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   };
 
   setup((const char*)a.A, a.lda, a.N, (const char*)a.B, a.ldb, a.T);
-  run(I8Slices{}, a.K);
+  run(I8Slices{}, a.K, few_setup);
 
   const int lrow = 4 * (lane >> 4);  // first of the 4 channels a lane holds
   const int lcol = lane & 15;        // token within a 16-wide block
@@ -278,32 +399,80 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int64_t t = n0 + wn0 + j * 16 + lcol;
-      sxv[j] = (t < a.T) ? a.sx[t] : 0.0f;
+      // clamped, unconditional loads: all in flight together
+      const float v = a.sx[t < a.T ? t : a.T - 1];
+      sxv[j] = (t < a.T) ? v : 0.0f;
     }
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t f = m0 + wm0 + i * 16 + lrow + r;
-        const float sc = f < a.N ? a.SCB[f] * (1.0f / 16129.0f) : 0.0f;
+        const float sv = a.SCB[f < a.N ? f : a.N - 1];
+        const float sc = f < a.N ? sv * (1.0f / 16129.0f) : 0.0f;
         // int32 accumulator -> fp32 acc * sx * SCB / 127^2, in place
 #pragma unroll
         for (int j = 0; j < NI; ++j)
           acc[i][j][r] = __builtin_bit_cast(int, (float)acc[i][j][r] * (sxv[j] * sc));
       }
-    if (Kt > 0) {
+    if (MODE == MODE_FUSED_X && inloop) {
+      // the outlier products were summed per (channel row, token) in px:
+      // through LDS into the accumulator layout.  The window's last columns
+      // go out, shifted to the bottom, with zeros up to the 32-column pad.
+      if (lane < BM) {
+        const int rem = (int)(n_use & 63);
+        if (rem > 0) {
+          wb_shift(2 * WB - rem);
+          wb_store(n_use - rem, round_up(n_use, 32));
+        }
+      }
+      __syncthreads();          // done with the int8 slices
+      float* sp = (float*)lds;  // [BM][BN]
+      if (lane < BM) {
+#pragma unroll
+        for (int t = 0; t < PX; ++t) sp[lane * BN + t] = px[t];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = wm0 + i * 16 + lrow + r, t = wn0 + j * 16 + lcol;
+            // the element goes through a scalar first: clang's bit_cast of
+            // a vector element reads element 0
+            const int bits = acc[i][j][r];
+            acc[i][j][r] = __builtin_bit_cast(int, __builtin_bit_cast(float, bits) + sp[row * BN + t]);
+          }
+    } else if (Kt > 0) {
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();  // every wave is done with the int8 slices
       setup((const char*)a.Wo, a.ldo * 2, a.N, (const char*)a.Xo, a.ldo * 2, a.T);
-      run(F16Slices{}, Kt);
+      run(F16Slices{}, Kt, [] {});
     }
     const bool yvec = ((a.N & 3) == 0) && ((((uintptr_t)a.Y) & 7) == 0);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int64_t f = m0 + wm0 + i * 16 + lrow;  // 4 consecutive channels
       float bv[4];
+      if constexpr (MODE == MODE_FUSED_X) {
+        // short kernels: clamped, unconditional loads, all four in flight
+        // together (the wide tiles keep the conditional form below, with
+        // which they do not spill in the K loop)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bv[r] = (a.bias && f + r < a.N) ? h2f(a.bias[f + r]) : 0.0f;
+        for (int r = 0; r < 4; ++r) bv[r] = 0.0f;
+        if (a.bias) {
+          _Float16 hv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hv[r] = a.bias[f + r < a.N ? f + r : a.N - 1];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bv[r] = f + r < a.N ? h2f(hv[r]) : 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bv[r] = (a.bias && f + r < a.N) ? h2f(a.bias[f + r]) : 0.0f;
+      }
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int64_t t = n0 + wn0 + j * 16 + lcol;
@@ -327,15 +496,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
 }
 
 namespace {
-template <int BM, int BN, int WM, int WN, int S, int KB, int MODE>
+template <int BM, int BN, int WM, int WN, int S, int KB, int MODE, bool NTA = false>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  constexpr size_t LDS = (size_t)S * (BM + BN) * KB;
-  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_i8<BM, BN, WM, WN, S, KB, MODE>,
+  constexpr size_t LDS = (size_t)S * (BM + BN) * KB + (MODE == MODE_FUSED_X ? few_lds(BN) : 0);
+  auto kern = k_gemm_i8<BM, BN, WM, WN, S, KB, MODE, NTA>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
   if (e != hipSuccess) return e;
   const int64_t ntiles = ceil_div(a.N, BM) * ceil_div(a.T, BN);
-  k_gemm_i8<BM, BN, WM, WN, S, KB, MODE><<<dim3((unsigned)ntiles), dim3(NT), LDS, st>>>(a);
+  kern<<<dim3((unsigned)ntiles), dim3(NT), LDS, st>>>(a);
   return hipGetLastError();
 }
 
@@ -358,6 +528,14 @@ int cu_count() {
 // waves, and B 512 tiles, 2 full waves.
 template <int MODE>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
+  // Few tokens: one wave a workgroup, a thin tile (32 or 64 channels x 16 or
+  // 32 tokens), three 128-byte slices in flight, weight loads non-temporal.
+  // Three slices rather than four keep 7 (32 x 16) or 3 (64 x 32) workgroups
+  // on a CU (LDS-bound), so that the 175B-width decode shapes (N = 49152)
+  // run in a single wave of workgroups.
+  constexpr int FM = MODE == MODE_FUSED ? MODE_FUSED_X : MODE;
+  if (a.T <= 16) return launch_cfg<32, 16, 32, 16, 3, 128, FM, true>(a, st);
+  if (a.T <= kFewT) return launch_cfg<64, 32, 64, 32, 3, 128, FM, true>(a, st);
   const int64_t cus = cu_count();
   auto cost = [&](int64_t bm, int64_t bn) {
     return ceil_div(ceil_div(a.N, bm) * ceil_div(a.T, bn), cus) * bm * bn;
@@ -368,10 +546,12 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
 }  // namespace
 
 bool gemm_i8_supported(const GemmArgs& a) {
-  // 16-byte aligned rows, and every operand addressable with 31-bit offsets
+  // 16-byte aligned rows and operands (Wo, Xo null for the int32 product),
+  // every operand addressable with 31-bit offsets
   const int64_t lim = (int64_t)1 << 31;
   return (a.K % 16 == 0) && (a.lda % 16 == 0) && (a.ldb % 16 == 0) &&
          ((((uintptr_t)a.A) & 15) == 0) && ((((uintptr_t)a.B) & 15) == 0) &&
+         ((((uintptr_t)a.Wo) & 15) == 0) && ((((uintptr_t)a.Xo) & 15) == 0) &&
          ((a.ldo * 2) % 16 == 0) && a.N * a.lda < lim && a.T * a.ldb < lim &&
          a.N * a.ldo * 2 < lim && a.T * a.ldo * 2 < lim;
 }

@@ -59,7 +59,7 @@ struct GemmArgs {
   const _Float16* Xo;
   int64_t ldo;
   const int32_t* counts;
-  const int32_t* O;  // ascending outlier list (the few-token kernel)
+  const int32_t* O;  // ascending outlier list (few-token calls)
   int64_t max_o;
   const _Float16* bias;
   _Float16* Y;
@@ -77,13 +77,10 @@ bool gemm_i8_supported(const GemmArgs& a);
 hipError_t launch_gemm_i8_fused(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_i8_s32(const GemmArgs& a, hipStream_t st);
 
-// Few tokens (1 <= T <= kGemvMaxT), 16-byte aligned operands: a kernel that
-// streams CB once.  It extracts the outlier weights itself for outlier sets
-// of at most kGemvOcap columns (the step-2 kernel then skips Wo).
-constexpr int64_t kGemvMaxT = 32;
-constexpr int64_t kGemvOcap = 128;
-bool gemv_i8_supported(const GemmArgs& a);
-hipError_t launch_gemv_i8_fused(const GemmArgs& a, hipStream_t st);
-hipError_t launch_gemv_i8_s32(const GemmArgs& a, hipStream_t st);
+// Few tokens (1 <= T <= kFewT, aligned operands): launch_gemm_i8_* run thin
+// tiles with one token tile, and the fused one extracts the outlier weights of
+// sets of at most kFewOcap columns itself (the step-2 kernel then skips Wo).
+constexpr int64_t kFewT = 32;
+constexpr int64_t kFewOcap = 128;
 
 }  // namespace i8mm

@@ -128,18 +128,34 @@ def test_wide_channel_tile(i8):
 @pytest.mark.parametrize("T,K,N,planted", [(1, 1040, 70, 3), (5, 1040, 70, 40), (32, 2048, 1000, 6),
                                             (17, 12288, 300, 12)])
 def test_few_tokens(i8, T, K, N, planted):
-    # T <= 32 runs the streaming product kernel, which picks the outlier
-    # weights out of the CB bytes it streams; an outlier in the last, partial
-    # 64-byte k-step exercises the K tail
+    # T <= 32 runs the few-token tiles, which pick the outlier weights out of
+    # the CB bytes they stage; an outlier in the last, partial slice of K
+    # exercises the K tail
     d = make_random_case(T * 11 + K + N, T, K, N, n_planted=planted, bias=True)
     X = d["X"].copy()
     X[0, K - 1] = 9.0
     _full_check(i8, X, d["W"], d["bias"], 6.0, f"few tokens {T}x{K}x{N}")
 
 
+@pytest.mark.parametrize("T,n,seed", [(1, 63, 76), (9, 64, 181), (16, 65, 273), (32, 100, 516),
+                                       (3, 128, 167), (20, 128, 389)])
+def test_few_tokens_outlier_window(i8, T, n, seed):
+    # the few-token tiles extract up to 128 outlier columns themselves; each
+    # lane keeps the last 64 values of its Wo row in registers and stores
+    # them after the K loop (and at every 64th column inside it), so n_o of
+    # 63, 64, 65, 100 and 128 cover a partial window, a full one, one flush
+    # plus a remainder and two flushes; K = 2064 ends in a 16-byte slice
+    K, N = 2064, 200
+    d = make_random_case(seed, T, K, N, n_planted=n - 1, bias=True)
+    X = d["X"].copy()
+    X[0, K - 1] = 9.0
+    assert len(O.find_outliers(X, 6.0)) == n
+    _full_check(i8, X, d["W"], d["bias"], 6.0, f"few tokens {T}x{K}x{N}, n_o={n}")
+
+
 def test_few_tokens_wide_outlier_set(i8):
-    # more outlier columns than the streaming kernel extracts itself (128):
-    # it takes Wo from the workspace, built by the step-2 kernel
+    # more outlier columns than the few-token tiles extract themselves (128):
+    # they take Wo from the workspace, built by the step-2 kernel
     d = make_random_case(907, 16, 2048, 300, n_planted=0, bias=True)
     n = len(O.find_outliers(d["X"], 2.5))
     assert n > 128

@@ -174,8 +174,9 @@ GEMM_SHAPES = [(16, 64, 64), (300, 517, 1024), (257, 300, 1000), (1, 1, 1), (5, 
                # large enough for the 320-channel tile (2 full waves of
                # workgroups instead of 2.5), with a ragged last channel tile
                (2048, 20380, 320),
-               # few tokens (the streaming kernel): ragged channels, K not a
-               # multiple of its 64-byte step, one and two 16-token blocks
+               # few tokens (the thin tiles): ragged channels, K not a
+               # multiple of the 128-byte slice, both tile shapes (T <= 16
+               # and T <= 32)
                (32, 1000, 4160), (17, 517, 1040), (1, 33, 16), (9, 4096, 12288), (4, 40, 0)]
 
 
