@@ -181,9 +181,11 @@ def main() -> int:
     ldq = -(-K // 64) * 64
     if T <= 32:
         # few tokens: the product streams CB once -- an HBM-bound kernel;
-        # algorithmic bytes per launch: CB, Xq, Xo, Y (and the outlier CB
-        # bytes it picks from the same stream)
-        gemm_bytes = N * K + T * ldq + 2 * T * n_pad + 2 * T * N
+        # algorithmic bytes per launch: reads CB, Xq, Xo, SCB, sx, bias;
+        # writes Y and the outlier weights Wo (picked out of the CB stream
+        # for up to 128 outlier columns, else read back from step 2's Wo)
+        gemm_bytes = (N * K + T * ldq + 2 * T * n_pad + 4 * N + 4 * T
+                      + (2 * N if d["bias"] is not None else 0) + 2 * N * n_pad + 2 * T * N)
         achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
