@@ -42,6 +42,19 @@ def kernel_fingerprint() -> str:
     return h.hexdigest()[:16]
 
 
+WORKLOAD_DESC = {
+    "tiny": "tiny (16 tokens, 64 x 64 LLM.int8() linear)",
+    "6.7b": "6.7b-scale first FF layer (LLM.int8() linear)",
+    "13b": "13b-scale first FF layer (LLM.int8() linear)",
+    "13b-down": "13b-scale second FF layer, down projection K = 4h (LLM.int8() linear)",
+    "13b-attn": "13b-scale attention projection K = N = h (LLM.int8() linear)",
+    "175b": "175b-scale first FF layer (LLM.int8() linear)",
+    "decode1": "decode1-scale first FF layer (LLM.int8() linear)",
+    "decode8": "decode8-scale first FF layer (LLM.int8() linear)",
+    "decode32": "decode32-scale first FF layer (LLM.int8() linear)",
+}
+
+
 def read_traffic(workload: str):
     """HBM bytes per launch of the product kernel from the committed counter
     summary, or None when it is missing or was taken on other kernel source."""
@@ -217,9 +230,10 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}-scale first FF layer (LLM.int8() linear)",
+        "config": {"workload": WORKLOAD_DESC.get(args.workload, args.workload),
                    "T": T, "K": K, "N": N, "threshold": wl.threshold, "n_outliers": n_o,
-                   "bias": d["bias"] is not None, "buffer_copies": copies},
+                   "bias": d["bias"] is not None, "buffer_copies": copies,
+                   "k_splits": i8.workspace_layout(T, N, K)["splits"]},
         "roofline": roofline,
         "stages_ms": {"detect": round(stage_avg[0], 5), "quantize_gather": round(stage_avg[1], 5),
                       "product": round(stage_avg[2], 5), "whole_call": round(stage_avg[3], 5)},

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define I8MM_ABI_VERSION 2
+#define I8MM_ABI_VERSION 3
 
 typedef enum {
   I8MM_OK = 0,
@@ -65,6 +65,18 @@ const char* i8mm_status_string(i8mm_status s);
 
 /* I8MM_ABI_VERSION of the built library. */
 int i8mm_abi_version(void);
+
+/*
+ * Tuning and test control, process-wide: the number of workgroups that share
+ * each output tile of the int8 product at T > 32, each walking 1/splits of K
+ * (split K; the partial int32 sums are added exactly, so Y does not depend on
+ * it).  0 (the default) lets the library choose per shape -- it splits only
+ * when the output tiles cannot fill the GPU, e.g. K-heavy down projections.
+ * Values above 4, or above the 128-byte slices of K, are clamped.  Not
+ * synchronized with calls in flight on other host threads.  splits < 0 ->
+ * I8MM_ERR_INVALID_ARG.
+ */
+i8mm_status i8mm_set_split_override(int64_t splits);
 
 /*
  * Weight quantization (done once per weight, when it is moved to the GPU;
@@ -94,12 +106,21 @@ typedef struct {
   size_t xq;       /* int8[T][ldq]: quantized X, outlier and pad columns 0     */
   size_t xo;       /* fp16[T][ldo]: X[:, O], zero-padded to ldo                */
   size_t wo;       /* fp16[N][ldo]: fp16(CB[:, O] * SCB / 127), zero-padded    */
+  size_t part;     /* int32 partial accumulators of a K-split product: one    */
+                   /* tile of the product per split (0 bytes when splits == 1) */
   int64_t ldq;     /* row pitch of xq in bytes (K rounded up to 64)            */
   int64_t ldo;     /* row pitch of xo and wo in elements (max_outliers up to 32) */
+  int64_t splits;  /* workgroups that share each output tile of the product,  */
+                   /* each walking 1/splits of K (1: no split)                 */
   size_t total;    /* bytes the workspace must hold                            */
 } i8mm_ws_layout;
 
-/* Fill *out for a forward call of this shape.  max_outliers in [0, K]. */
+/*
+ * Fill *out for a forward call of this shape.  max_outliers in [0, K].
+ * The K split (and so the size) is chosen for the current device's compute
+ * unit count and the split override below; size the workspace on the
+ * device, and under the override, that the forward will run with.
+ */
 i8mm_status int8_linear_workspace_layout(int64_t T, int64_t N, int64_t K,
                                          int64_t max_outliers, i8mm_ws_layout* out);
 

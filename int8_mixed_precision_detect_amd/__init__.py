@@ -23,7 +23,7 @@ from ._lib import I8mmError, WsLayout, check, lib
 __all__ = [
     "I8mmError", "quantize_weight", "linear_forward", "workspace_layout", "workspace_size",
     "alloc_workspace", "linear_status", "find_outliers", "quantize_rows", "outlier_weights",
-    "gemm_s32", "profile_enable", "profile_read", "Int8Linear",
+    "gemm_s32", "profile_enable", "profile_read", "set_split_override", "Int8Linear",
 ]
 
 DEFAULT_THRESHOLD = 6.0
@@ -176,6 +176,12 @@ def gemm_s32(A: torch.Tensor, B: torch.Tensor, K: Optional[int] = None) -> torch
           lib().int8_gemm_s32(_ptr(A), A.shape[1], _ptr(B), B.shape[1], _ptr(C), T, N, K,
                               _stream(A)))
     return C
+
+
+def set_split_override(splits: int = 0) -> None:
+    """Workgroups per output tile of the product at T > 32 (split K); 0 = the
+    library's choice.  Process-wide; size workspaces under the same setting."""
+    check("i8mm_set_split_override", lib().i8mm_set_split_override(int(splits)))
 
 
 def profile_enable(on: bool = True) -> None:

@@ -24,8 +24,8 @@ c_float = ctypes.c_float
 class WsLayout(ctypes.Structure):
     _fields_ = [
         ("counts", c_size), ("outliers", c_size), ("mask", c_size), ("sx", c_size),
-        ("xq", c_size), ("xo", c_size), ("wo", c_size), ("ldq", c_i64), ("ldo", c_i64),
-        ("total", c_size),
+        ("xq", c_size), ("xo", c_size), ("wo", c_size), ("part", c_size),
+        ("ldq", c_i64), ("ldo", c_i64), ("splits", c_i64), ("total", c_size),
     ]
 
 
@@ -33,6 +33,7 @@ class WsLayout(ctypes.Structure):
 SIGNATURES = {
     "i8mm_status_string": (ctypes.c_char_p, [c_int]),
     "i8mm_abi_version": (c_int, []),
+    "i8mm_set_split_override": (c_int, [c_i64]),
     "int8_quantize_weight": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_ptr]),
     "int8_linear_workspace_layout": (c_int, [c_i64, c_i64, c_i64, c_i64, ctypes.POINTER(WsLayout)]),
     "int8_linear_workspace_size": (c_size, [c_i64, c_i64, c_i64, c_i64]),

@@ -42,6 +42,9 @@ i8mm_status layout_of(int64_t T, int64_t N, int64_t K, int64_t max_o, i8mm_ws_la
   L->xq = take((size_t)T * (size_t)L->ldq);
   L->xo = take((size_t)T * (size_t)L->ldo * 2);
   L->wo = take((size_t)N * (size_t)L->ldo * 2);
+  const GemmPlan gp = plan_gemm_i8(T, N, K);
+  L->part = take((size_t)gp.part_elems * 4);
+  L->splits = gp.splits;
   L->total = off;
   return I8MM_OK;
 }
@@ -74,6 +77,12 @@ const char* i8mm_status_string(i8mm_status s) {
 }
 
 int i8mm_abi_version(void) { return I8MM_ABI_VERSION; }
+
+i8mm_status i8mm_set_split_override(int64_t splits) {
+  if (splits < 0) return I8MM_ERR_INVALID_ARG;
+  set_split_override(splits);
+  return I8MM_OK;
+}
 
 i8mm_status int8_quantize_weight(const void* W, int64_t N, int64_t K, int8_t* CB, float* SCB,
                                  hipStream_t stream) {
@@ -178,6 +187,10 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   a.max_o = max_outliers;
   a.bias = (const _Float16*)bias;
   a.Y = (_Float16*)Y;
+  const GemmPlan gp = plan_gemm_i8(T, N, K);
+  a.cfg = gp.cfg;
+  a.splits = gp.splits;
+  a.part = gp.part_elems > 0 ? (int32_t*)(w + L.part) : nullptr;
   // aligned operands: the tiled kernel (for few tokens it extracts small
   // outlier weight sets itself); otherwise the generic one
   const bool fast = gemm_i8_supported(a);
@@ -279,6 +292,7 @@ i8mm_status int8_gemm_s32(const int8_t* A, int64_t lda, const int8_t* B, int64_t
   if (!C || !aligned(C, 4) || (K > 0 && (!A || !B))) return I8MM_ERR_INVALID_ARG;
   (void)hipGetLastError();
   GemmArgs a{};
+  a.cfg = -1;  // the best unsplit tile configuration
   a.A = B;  // weight side (rows = output columns of C)
   a.lda = ldb;
   a.B = A;  // activation side (rows = rows of C)

@@ -34,6 +34,7 @@
 // applied on the global side: lane i fetches the chunk that belongs at its
 // LDS position.  Chunks past the end of K read as zeros (their offset points
 // past the buffer's range), so any K that is a multiple of 16 is exact.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -46,7 +47,10 @@ namespace {
 // MODE_FUSED_X: the fused product for few tokens (one token tile, one wave
 // owning every channel row of its tile), which also extracts the outlier
 // weights itself -- see the int8 loop.
-constexpr int MODE_I32 = 0, MODE_FUSED = 1, MODE_FUSED_X = 2;
+// Split K (MODE_PART then MODE_COMBINE): splits workgroups a tile each walk
+// a range of K and store their int32 accumulators in a.part; one combine
+// workgroup a tile loads and adds them (exact) and runs the fused epilogue.
+constexpr int MODE_I32 = 0, MODE_FUSED = 1, MODE_FUSED_X = 2, MODE_PART = 3, MODE_COMBINE = 4;
 // LDS beyond the slices for MODE_FUSED_X: the outlier list and the tile's
 // X[:, O] values ([kFewOcap][BN] halves)
 constexpr size_t few_lds(int BN) { return (size_t)kFewOcap * 4 + (size_t)kFewOcap * BN * 2; }
@@ -86,7 +90,7 @@ __device__ __forceinline__ void wait_lgkm0() {
 }  // namespace
 
 // NTA: the weight operand's slice loads are non-temporal (streamed once: the
-// few-token shapes, where each weight byte is used by one workgroup)
+// few-token shapes, where each weight byte is used by one workgroup).
 template <int BM, int BN, int WM, int WN, int S, int KB, int MODE, bool NTA>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs a) {
   // The body uses amdgcn-only types (buffer resources); the host pass only
@@ -108,14 +112,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / NWN) * WM, wn0 = (wave % NWN) * WN;
 
-  // tile order: workgroups are dealt to the 8 XCDs round-robin; give each XCD
-  // a contiguous run of tiles, consecutive tiles sharing one weight tile.
+  // work items (split, tile), split-major.  Workgroups are dealt to the 8
+  // XCDs round-robin; give each XCD a contiguous run of items, consecutive
+  // tiles sharing one weight tile.
   const int64_t tiles_m = ceil_div(a.N, BM), tiles_n = ceil_div(a.T, BN);
   const int64_t ntiles = tiles_m * tiles_n;
+  const int64_t splits = MODE == MODE_PART ? a.splits : 1;
+  const int64_t items = ntiles * splits;
   int64_t bid = blockIdx.x;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-  const int64_t tn = bid % tiles_n, tm = bid / tiles_n;
+  if ((items & 7) == 0) bid = (bid & 7) * (items >> 3) + (bid >> 3);
+  const int64_t split = bid / ntiles, tile = bid % ntiles;
+  const int64_t tn = tile % tiles_n, tm = tile / tiles_n;
   const int64_t m0 = tm * BM, n0 = tn * BN;
+  // this split's range of K: whole slices, the last range ragged
+  const int64_t ksplit = round_up(ceil_div(a.K, splits), KB);
+  const int64_t kbeg = split * ksplit < a.K ? split * ksplit : a.K;
+  const int64_t kend = kbeg + ksplit < a.K ? kbeg + ksplit : a.K;
 
   // Slice loads: buffer_load_dwordx4 ... lds.  The operand is a buffer
   // resource (base in SGPRs), a lane's 32-bit offset (row * ld + its chunk)
@@ -165,9 +177,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
 #pragma unroll
       for (int u = 0; u < PW; ++u) dma(u, (void*)lds_dst(buf, u), voff[u], k0);
     } else {
+      const int rem = (int)(Kb - k0);  // bytes of the slice inside [k0, Kb)
 #pragma unroll
       for (int u = 0; u < PW; ++u)
-        dma(u, (void*)lds_dst(buf, u), (k0 + kc < Kb) ? voff[u] : 0x80000000u, k0);
+        dma(u, (void*)lds_dst(buf, u), kc < rem ? voff[u] : 0x80000000u, k0);
     }
   };
   // fragment of 16 rows at k-step h of a slice: lane -> row (lane & 15),
@@ -337,14 +350,33 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     }
   };
 
-  // K loop over Kb bytes of the operands set up last: S slices in flight,
-  // one barrier per slice.  LDS must be free of earlier readers on entry.
-  // primed() runs once the first slices are issued.
-  auto run = [&](auto f16, int64_t Kb, auto&& primed) {
-    const int64_t nk = ceil_div(Kb, KB);
+  // The fused epilogue's fp16 outlier operands (Xo/Wo rows of kt_f16 bytes):
+  // when they fit one slice (up to 64 outlier columns) that slice is issued
+  // into a slice buffer the int8 loop no longer needs, during its last
+  // slice, so that its latency overlaps the end of the loop and the scaling.
+  int64_t kt_f16 = 0;
+  if constexpr (MODE == MODE_FUSED || MODE == MODE_FUSED_X || MODE == MODE_COMBINE) {
+    const int64_t n_o = a.counts[0];
+    kt_f16 = round_up(n_o < a.max_o ? n_o : a.max_o, 32) * 2;
+  }
+  const bool tail_pre = (MODE == MODE_FUSED || MODE == MODE_COMBINE) && kt_f16 > 0 && kt_f16 <= KB;
+  int tail_buf = 0;
+  auto tail_prefetch = [&](int buf) {
+    setup((const char*)a.Wo, a.ldo * 2, a.N, (const char*)a.Xo, a.ldo * 2, a.T);
+    issue(buf, 0, kt_f16);
+    tail_buf = buf;
+  };
+
+  // K loop over bytes [kb, ke) of the operands set up last: S slices in
+  // flight, one barrier per slice.  LDS must be free of earlier readers on
+  // entry.  primed() runs once the first slices are issued.
+  // Slice kt goes to buffer (b0 + kt) % S; the first `pre` slices were
+  // issued before the call.
+  auto run = [&](auto f16, int64_t kb, int64_t Kb, auto&& primed, int b0 = 0, int pre = 0) {
+    const int64_t nk = ceil_div(Kb - kb, KB);
 #pragma unroll
     for (int s = 0; s < S; ++s)
-      if (s < nk) issue(s, s * KB, Kb);
+      if (s >= pre && s < nk) issue((b0 + s) % S, kb + s * KB, Kb);
     primed();
     for (int64_t kt = 0; kt < nk; ++kt) {
       // Slice kt must have landed.  Issued so far: slices up to
@@ -356,17 +388,54 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       // one barrier: slice kt is visible to every wave, and every wave is
       // done with slice kt-1, whose buffer is refilled with slice kt-1+S
       __builtin_amdgcn_s_barrier();
-      if (kt >= 1 && kt - 1 + S < nk) issue((int)((kt - 1) % S), (kt - 1 + S) * KB, Kb);
-      if constexpr (MODE == MODE_FUSED_X && !decltype(f16)::value) extract((int)(kt % S), kt * KB);
-      compute(f16, (int)(kt % S));
+      if (kt >= 1 && kt - 1 + S < nk) issue((int)((b0 + kt - 1) % S), kb + (kt - 1 + S) * KB, Kb);
+      if constexpr (MODE == MODE_FUSED && !decltype(f16)::value) {
+        // the last slice: buffer (kt + 1) % S held slice kt + 1 - S, done.
+        // (An opaque copy of the flag, so that the compiler does not version
+        // the whole loop on it.)
+        int pre = tail_pre && kt == nk - 1;
+        asm volatile("" : "+v"(pre));
+        if (__builtin_amdgcn_readfirstlane(pre)) tail_prefetch((int)((b0 + kt + 1) % S));
+      }
+      if constexpr (MODE == MODE_FUSED_X && !decltype(f16)::value)
+        extract((int)((b0 + kt) % S), kb + kt * KB);
+      compute(f16, (int)((b0 + kt) % S));
       // keeps the epilogue's loads (scales, bias) below the loop instead of
       // hoisted above it, where they would hold registers throughout
       asm volatile("" ::: "memory");
     }
   };
 
-  setup((const char*)a.A, a.lda, a.N, (const char*)a.B, a.ldb, a.T);
-  run(I8Slices{}, a.K, few_setup);
+  // int32 partial tiles of split K, in the accumulators' register layout:
+  // block (i, j) of wave w at ((w * MI + i) * NI + j) * 64 + lane, 16 bytes
+  // a lane (coalesced 1 KB per block)
+  auto part_at = [&](int64_t sp) {
+    return (v4i*)(a.part + (sp * ntiles + tile) * ((int64_t)BM * BN)) +
+           (int64_t)wave * (MI * NI * 64) + lane;
+  };
+  if constexpr (MODE == MODE_COMBINE) {
+    if (tail_pre) tail_prefetch(0);
+    // acc = the sum of the splits' partial tiles (exact int32)
+#pragma unroll
+    for (int64_t sp = 0; sp < a.splits; ++sp) {
+      const v4i* src = part_at(sp);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) acc[i][j] += src[(i * NI + j) * 64];
+    }
+  } else {
+    setup((const char*)a.A, a.lda, a.N, (const char*)a.B, a.ldb, a.T);
+    run(I8Slices{}, kbeg, kend, few_setup);
+  }
+  if constexpr (MODE == MODE_PART) {
+    v4i* dst = part_at(split);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) dst[(i * NI + j) * 64] = acc[i][j];
+    return;
+  }
 
   const int lrow = 4 * (lane >> 4);  // first of the 4 channels a lane holds
   const int lcol = lane & 15;        // token within a 16-wide block
@@ -392,9 +461,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     }
   } else {
     // ---- fused epilogue ----
-    const int64_t n_o = a.counts[0];
-    const int64_t n_use = n_o < a.max_o ? n_o : a.max_o;
-    const int64_t Kt = round_up(n_use, 32) * 2;  // bytes of an Xo / Wo row in use
+    const int64_t Kt = kt_f16;  // bytes of an Xo / Wo row in use
     float sxv[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
@@ -446,10 +513,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
             acc[i][j][r] = __builtin_bit_cast(int, __builtin_bit_cast(float, bits) + sp[row * BN + t]);
           }
     } else if (Kt > 0) {
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();  // every wave is done with the int8 slices
-      setup((const char*)a.Wo, a.ldo * 2, a.N, (const char*)a.Xo, a.ldo * 2, a.T);
-      run(F16Slices{}, Kt, [] {});
+      if (!tail_pre) {
+        wait_lgkm0();
+        __builtin_amdgcn_s_barrier();  // every wave is done with the int8 slices
+        setup((const char*)a.Wo, a.ldo * 2, a.N, (const char*)a.Xo, a.ldo * 2, a.T);
+      }
+      // (prefetched: its one slice is in flight in buffer tail_buf)
+      run(F16Slices{}, 0, Kt, [] {}, tail_buf, tail_pre ? 1 : 0);
     }
     const bool yvec = ((a.N & 3) == 0) && ((((uintptr_t)a.Y) & 7) == 0);
 #pragma unroll
@@ -504,8 +574,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
   if (e != hipSuccess) return e;
-  const int64_t ntiles = ceil_div(a.N, BM) * ceil_div(a.T, BN);
-  kern<<<dim3((unsigned)ntiles), dim3(NT), LDS, st>>>(a);
+  const int64_t items = ceil_div(a.N, BM) * ceil_div(a.T, BN) * (MODE == MODE_PART ? a.splits : 1);
+  kern<<<dim3((unsigned)items), dim3(NT), LDS, st>>>(a);
   return hipGetLastError();
 }
 
@@ -517,33 +587,99 @@ int cu_count() {
   return n;
 }
 
-// Tile configurations (channels x tokens per workgroup, per wave, slices
-// in flight, slice bytes per row), one workgroup per CU (LDS-bound):
-//   A: 256 x 256, 8 waves of 64 x 128, two 128-byte slices (128 KB LDS)
-//   B: 320 x 256, 8 waves of 80 x 128, two 128-byte slices (144 KB LDS)
-// The workgroups run in waves of one per CU, so a launch costs about
-// ceil(tiles / CUs) times the time of one tile.  The host takes the
-// configuration with the smaller ceil(tiles / CUs) * tile area (ties go to
-// A): on the 13B-scale layer (20480 x 2048 outputs) A needs 640 tiles, 2.5
-// waves, and B 512 tiles, 2 full waves.
+std::atomic<int64_t> g_split_override{0};
+
+// Tile configurations of the wide tiles (channels x tokens per workgroup,
+// per wave, slices in flight, slice bytes per row), one workgroup per CU
+// (LDS-bound):
+//   0: 320 x 256, 8 waves of 80 x 128, two 128-byte slices (144 KB LDS)
+//   1: 256 x 256, 8 waves of 64 x 128, two 128-byte slices (128 KB LDS)
+constexpr int64_t kCfgBM[2] = {320, 256}, kCfgBN[2] = {256, 256};
+constexpr int64_t kMaxSplits = 4;
+constexpr int64_t kMinSplitK = 1024;  // bytes of K a split walks at least
+
+// The workgroups run in waves of one per CU, and a workgroup's time is about
+// its tile area times the 128-byte slices of K it walks, so a launch costs
+// about ceil(tiles * splits / CUs) * area * ceil(slices / splits), with 5 %
+// added for the exchange of partial sums (a second launch) when K is split.  The host takes
+// the cheapest (ties: fewer splits, then configuration 1).  The 13B-scale
+// layer (20480 x 2048 outputs, K = 5120) runs 512 tiles of configuration 0
+// in two full waves (configuration 1 would need 640 tiles, 2.5 waves); the
+// 13B down projection (5120 x 2048 outputs, K = 20480) has only 128 tiles,
+// so K is split in two: 256 workgroups, one full wave.
+void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split, int64_t* cfg,
+                 int64_t* splits) {
+  const int64_t cus = cu_count();
+  const int64_t slices = ceil_div(K, 128) > 0 ? ceil_div(K, 128) : 1;
+  const int64_t ovr = allow_split ? g_split_override.load() : 1;
+  // an override is clamped to [1, min(slices, kMaxSplits)]
+  int64_t want = ovr < slices ? ovr : slices;
+  want = want < kMaxSplits ? want : kMaxSplits;
+  double best = 0.0;
+  *cfg = 1;
+  *splits = 1;
+  bool first = true;
+  for (int64_t sp = 1; sp <= kMaxSplits; ++sp) {
+    if (ovr > 0 && sp != want) continue;
+    if (ovr == 0 && sp > 1 && (ceil_div(K, sp) < kMinSplitK || sp > slices)) continue;
+    for (int c = 1; c >= 0; --c) {
+      const int64_t tiles = ceil_div(N, kCfgBM[c]) * ceil_div(T, kCfgBN[c]);
+      const double cost = (double)ceil_div(tiles * sp, cus) * (double)(kCfgBM[c] * kCfgBN[c]) *
+                          (double)ceil_div(slices, sp) * (sp > 1 ? 1.05 : 1.0);
+      if (first || cost < best) {
+        best = cost;
+        *cfg = c;
+        *splits = sp;
+        first = false;
+      }
+    }
+  }
+}
+
 template <int MODE>
-hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_mode(const GemmArgs& a0, hipStream_t st) {
   // Few tokens: one wave a workgroup, a thin tile (32 or 64 channels x 16 or
   // 32 tokens), three 128-byte slices in flight, weight loads non-temporal.
   // Three slices rather than four keep 7 (32 x 16) or 3 (64 x 32) workgroups
   // on a CU (LDS-bound), so that the 175B-width decode shapes (N = 49152)
   // run in a single wave of workgroups.
   constexpr int FM = MODE == MODE_FUSED ? MODE_FUSED_X : MODE;
-  if (a.T <= 16) return launch_cfg<32, 16, 32, 16, 3, 128, FM, true>(a, st);
-  if (a.T <= kFewT) return launch_cfg<64, 32, 64, 32, 3, 128, FM, true>(a, st);
-  const int64_t cus = cu_count();
-  auto cost = [&](int64_t bm, int64_t bn) {
-    return ceil_div(ceil_div(a.N, bm) * ceil_div(a.T, bn), cus) * bm * bn;
-  };
-  if (cost(320, 256) < cost(256, 256)) return launch_cfg<320, 256, 80, 128, 2, 128, MODE>(a, st);
+  if (a0.T <= 16) return launch_cfg<32, 16, 32, 16, 3, 128, FM, true>(a0, st);
+  if (a0.T <= kFewT) return launch_cfg<64, 32, 64, 32, 3, 128, FM, true>(a0, st);
+  GemmArgs a = a0;
+  if (MODE != MODE_FUSED || a.splits < 1 || !a.part) a.splits = 1;
+  int64_t cfg = a.cfg, sp = 1;
+  if (cfg < 0 || cfg > 1) {  // no plan: the best unsplit configuration
+    choose_wide(a.T, a.N, a.K, false, &cfg, &sp);
+    a.splits = 1;
+  }
+  if constexpr (MODE == MODE_FUSED) {
+    if (a.splits > 1) {  // split K: partial tiles, then one combine launch
+      hipError_t e;
+      if (cfg == 0) {
+        e = launch_cfg<320, 256, 80, 128, 2, 128, MODE_PART>(a, st);
+        return e != hipSuccess ? e : launch_cfg<320, 256, 80, 128, 2, 128, MODE_COMBINE>(a, st);
+      }
+      e = launch_cfg<256, 256, 64, 128, 2, 128, MODE_PART>(a, st);
+      return e != hipSuccess ? e : launch_cfg<256, 256, 64, 128, 2, 128, MODE_COMBINE>(a, st);
+    }
+  }
+  if (cfg == 0) return launch_cfg<320, 256, 80, 128, 2, 128, MODE>(a, st);
   return launch_cfg<256, 256, 64, 128, 2, 128, MODE>(a, st);
 }
 }  // namespace
+
+void set_split_override(int64_t splits) { g_split_override.store(splits > 0 ? splits : 0); }
+int64_t split_override() { return g_split_override.load(); }
+
+GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K) {
+  GemmPlan p{-1, 1, 0, 0};
+  if (T <= kFewT || K % 16 != 0 || K <= 0) return p;
+  choose_wide(T, N, K, true, &p.cfg, &p.splits);
+  p.tiles = ceil_div(N, kCfgBM[p.cfg]) * ceil_div(T, kCfgBN[p.cfg]);
+  if (p.splits > 1) p.part_elems = p.splits * p.tiles * kCfgBM[p.cfg] * kCfgBN[p.cfg];
+  return p;
+}
 
 bool gemm_i8_supported(const GemmArgs& a) {
   // 16-byte aligned rows and operands (Wo, Xo null for the int32 product),

@@ -65,6 +65,13 @@ struct GemmArgs {
   _Float16* Y;
   // int32 output instead of the epilogue
   int32_t* C;
+  // split K (fused product only): `splits` workgroups a tile each walk a
+  // contiguous range of K and store their int32 accumulators in `part`
+  // (splits x tiles x BM x BN); a second launch adds them and runs the
+  // epilogue.
+  int64_t splits;
+  int64_t cfg;  // tile configuration of the plan (see plan_gemm_i8); -1: choose
+  int32_t* part;
 };
 
 // Any shape and alignment: register-staged, byte-granular loads.
@@ -74,6 +81,19 @@ hipError_t launch_gemm_s32(const GemmArgs& a, hipStream_t st);
 // 16-byte aligned operands (K, lda, ldb multiples of 16): the pipelined
 // gfx950 kernel.
 bool gemm_i8_supported(const GemmArgs& a);
+// The tile configuration and K split the fused product takes for a shape on
+// this device, and the workspace it needs for them.
+struct GemmPlan {
+  int64_t cfg;         // tile configuration (few-token tiles: -1)
+  int64_t splits;      // 1: no split
+  int64_t tiles;       // output tiles
+  int64_t part_elems;  // int32 elements of partial accumulators
+};
+GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K);
+// Process-wide override of the K split (0: the plan's own choice); a test
+// and tuning control.
+void set_split_override(int64_t splits);
+int64_t split_override();
 hipError_t launch_gemm_i8_fused(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_i8_s32(const GemmArgs& a, hipStream_t st);
 

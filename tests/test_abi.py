@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.i8mm_abi_version() == 2
+    assert L.i8mm_abi_version() == 3
     for code, name in [(0, b"I8MM_OK"), (1, b"I8MM_ERR_INVALID_ARG"), (2, b"I8MM_ERR_WORKSPACE"),
                        (3, b"I8MM_ERR_UNSUPPORTED"), (4, b"I8MM_ERR_HIP"),
                        (5, b"I8MM_ERR_OUTLIER_OVERFLOW")]:
@@ -58,10 +58,11 @@ def test_workspace_layout(L):
                         (7, 5, 3, 0), (0, 4, 8, 8)]:
         lay = WsLayout()
         assert L.int8_linear_workspace_layout(T, N, K, mo, ctypes.byref(lay)) == 0
+        assert lay.splits == 1  # these shapes fill the GPU without splitting K
         regions = [("counts", 16), ("outliers", max(mo, 1) * 4),
                    ("mask", max(math.ceil(K / 32), 1) * 4),
                    ("sx", T * 4), ("xq", T * lay.ldq), ("xo", T * lay.ldo * 2),
-                   ("wo", N * lay.ldo * 2)]
+                   ("wo", N * lay.ldo * 2), ("part", 0)]
         end = 0
         for name, size in regions:
             off = getattr(lay, name)
@@ -72,6 +73,33 @@ def test_workspace_layout(L):
         assert lay.ldq % 64 == 0 and lay.ldq >= K
         assert lay.ldo % 32 == 0 and lay.ldo >= mo
         assert L.int8_linear_workspace_size(T, N, K, mo) == lay.total
+
+
+def test_split_k_layout(L):
+    # K-heavy down projection (13B: 5120 x 2048 outputs, K = 20480): 128
+    # output tiles of 320 x 256 cannot fill 256 compute units, so K is split
+    # in two; the workspace gains one int32 partial tile per split and tile.
+    # (Without a GPU the planner assumes 256 compute units.)
+    from int8_mixed_precision_detect_amd._lib import WsLayout
+    T, N, K = 2048, 5120, 20480
+    lay = WsLayout()
+    assert L.int8_linear_workspace_layout(T, N, K, K, ctypes.byref(lay)) == 0
+    assert lay.splits == 2
+    tiles = (N // 320) * (T // 256)
+    assert lay.total - lay.part >= 2 * tiles * 320 * 256 * 4
+    assert lay.part >= lay.wo + N * lay.ldo * 2
+    # the override: clamped to 4, 0 restores the planner's choice
+    try:
+        for want, got in [(1, 1), (3, 3), (9, 4)]:
+            assert L.i8mm_set_split_override(want) == 0
+            assert L.int8_linear_workspace_layout(T, N, K, K, ctypes.byref(lay)) == 0
+            assert lay.splits == got
+            assert (lay.total > lay.wo + N * lay.ldo * 2 + 4096) == (got > 1)
+        assert L.i8mm_set_split_override(-1) == 1
+    finally:
+        assert L.i8mm_set_split_override(0) == 0
+    assert L.int8_linear_workspace_layout(T, N, K, K, ctypes.byref(lay)) == 0
+    assert lay.splits == 2
 
 
 def test_invalid_arguments_are_rejected_on_the_host(L):

@@ -185,6 +185,35 @@ def test_k_zero_gives_bias(i8):
     assert np.all(host(Y) == 0)
 
 
+@pytest.mark.parametrize("T,K,N,planted", [(300, 4112, 700, 5), (513, 2048, 777, 40),
+                                            (40, 1040, 300, 3), (257, 256, 64, 2)])
+def test_split_k_is_bit_identical(i8, T, K, N, planted):
+    # split K: each split's workgroups store int32 partial tiles, a second
+    # launch adds them (exact) and runs the same epilogue, so Y and the
+    # intermediates must not depend on the split.  K = 4112 ends in a partial
+    # slice; K = 256 has two slices, so 3 and 4 splits clamp to 2.
+    d = make_random_case(T + K + N, T, K, N, n_planted=planted, bias=True)
+    outs = []
+    try:
+        for sp in (1, 2, 3, 4):
+            i8.set_split_override(sp)
+            lay = i8.workspace_layout(T, N, K)
+            assert lay["splits"] == min(sp, -(-K // 128))
+            Y, _, _ = _full_check(i8, d["X"], d["W"], d["bias"], 6.0,
+                                     f"split K x{sp} {T}x{K}x{N}")
+            outs.append(host(Y).view(np.uint16))
+    finally:
+        i8.set_split_override(0)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+def test_down_projection_plans_a_split(i8):
+    # 13B down projection: 128 output tiles for 256 compute units
+    lay = i8.workspace_layout(2048, 5120, 20480)
+    assert lay["splits"] == 2
+
+
 def test_outlier_overflow_is_reported(i8):
     d = make_random_case(904, 64, 256, 64, n_planted=10)
     say("forward overflow")
@@ -244,7 +273,8 @@ def _sampled_check(i8, name, n_rows=48, n_cols=384, cache={}):
     return n
 
 
-@pytest.mark.parametrize("name", ["6.7b", "13b", "175b", "decode1", "decode8", "decode32"])
+@pytest.mark.parametrize("name", ["6.7b", "13b", "13b-down", "13b-attn", "175b", "decode1",
+                                  "decode8", "decode32"])
 def test_full_size_workload_sampled(i8, name):
     n = _sampled_check(i8, name)
     if name != "175b":

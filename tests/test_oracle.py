@@ -333,7 +333,7 @@ def test_planted_mistake_is_caught(mutation, monkeypatch):
 def test_planted_columns_are_the_outliers():
     """Under N(0,1) the chance of a natural |x| >= 6 is ~2e-9 per element, so
     on the unit-sigma workloads the outlier set is exactly the planted one."""
-    for name in ("tiny", "6.7b", "13b", "decode1", "decode8", "decode32"):
+    for name in ("tiny", "6.7b", "13b", "13b-down", "13b-attn", "decode1", "decode8", "decode32"):
         d = make_inputs(name, with_weight=False)
         got = O.find_outliers(d["X"], d["threshold"])
         assert np.array_equal(got, np.sort(d["planted"])), name

@@ -7,9 +7,11 @@ oracle and the HIP path take their inputs from here, byte for byte.
 The shapes stand in for the first feed-forward layer of decoder models whose
 intermediate width is four times the model width (the speed study in the
 "INT8演算による速度改善" section of the zenn.dev summary of the LLM.int8()
-paper), and the planted outlier columns follow that page's "outlierは極めて
-"系統的"に出現する" section (about 0.1 % of hidden dims carry the outliers at
-6.7B scale).  No dataset, model or trained weight is used.
+paper), plus, at 13B width, the second feed-forward layer (K = 4h, N = h)
+and an attention projection (K = N = h) of the same block; the planted
+outlier columns follow that page's "outlierは極めて"系統的"に出現する"
+section (about 0.1 % of hidden dims carry the outliers at 6.7B scale).  No
+dataset, model or trained weight is used.
 
 Recipe (one ``numpy.random.default_rng(seed)`` stream, PCG64, drawn in this
 order): X base ~ N(0, sigma) -> outlier column indices (``rng.choice``
@@ -56,6 +58,10 @@ WORKLOADS = {
     "6.7b": Workload("6.7b", 2048, 4096, 16384, 1.0, 4, 6.0, 60.0, 0.2, 0.02, None),
     "13b": Workload("13b", 2048, 5120, 20480, 1.0, 6, 6.0, 60.0, 1.0, 0.02, 0.01),
     "175b": Workload("175b", 4096, 12288, 49152, 1.5, 12, 6.0, 80.0, 1.0, 0.015, None),
+    # the rest of a 13B block: the second FF layer (down projection, K = 4h,
+    # N = h) and an attention projection (K = N = h); same activation recipe
+    "13b-down": Workload("13b-down", 2048, 20480, 5120, 1.0, 20, 6.0, 60.0, 1.0, 0.01, 0.01),
+    "13b-attn": Workload("13b-attn", 2048, 5120, 5120, 1.0, 6, 6.0, 60.0, 1.0, 0.02, 0.01),
     # decode sweep: the 175B layer's weight, T tokens of activations
     "decode1": Workload("decode1", 1, 12288, 49152, 1.0, 12, 6.0, 80.0, 1.0, 0.015, None),
     "decode8": Workload("decode8", 8, 12288, 49152, 1.0, 12, 6.0, 80.0, 1.0, 0.015, None),
