@@ -206,9 +206,12 @@ def main() -> int:
                     "avg_ms": round(gemm_ms, 5), "algorithmic_bytes_per_launch": gemm_bytes}
     else:
         achieved = ops / (gemm_ms * 1e-3) / 1e12
+        splits = i8.workspace_layout(T, N, K)["splits"]
+        kname = ("k_gemm_i8 (fused int8 product + epilogue)" if splits == 1 else
+                 f"k_gemm_i8, K split {splits} ways (int8 partial tiles, then combine + epilogue)")
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
-                    "traffic": traffic, "kernel": "k_gemm_i8 (fused int8 product + epilogue)",
+                    "traffic": traffic, "kernel": kname,
                     "avg_ms": round(gemm_ms, 5), "algorithmic_ops_per_launch": ops}
     detect_bytes = 2.0 * T * K
     # step-2 prep: read X, write Xq (ldq = K rounded to 64), sx and Xo; the
