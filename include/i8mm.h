@@ -161,6 +161,26 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K,
                                 hipStream_t stream);
 
 /*
+ * The layer with the fp16 weight kept (the pages' Linear8bitLt interface has
+ * a has_fp16_weights flag; this is the True side of it, in the reading that
+ * the layer then quantizes W on every call and takes the outlier weight dims
+ * from W itself):
+ *
+ *   CB, SCB = int8_quantize_weight(W)            (written to CB/SCB)
+ *   Wo      = W[:, O]                            (exact, no CB round trip)
+ *   Y       = as int8_linear_forward with that Wo
+ *
+ *   W   : fp16 [N, K], 2-byte aligned
+ *   CB  : int8 [N, K] out (overwritten every call), SCB : fp32 [N] out
+ * Other arguments, the workspace and the errors as int8_linear_forward.
+ * K == 0 gives Y = bias (or 0) and leaves CB/SCB unwritten.
+ */
+i8mm_status int8_linear_forward_fp16w(const void* X, int64_t T, int64_t K, const void* W,
+                                      int64_t N, const void* bias, float threshold, int8_t* CB,
+                                      float* SCB, void* Y, void* ws, size_t ws_bytes,
+                                      int64_t max_outliers, hipStream_t stream);
+
+/*
  * Synchronizes `stream`, then reads the counts of the last forward call that
  * used `ws`: *n_outliers = number of outlier columns found (may exceed
  * max_outliers).  Returns I8MM_ERR_OUTLIER_OVERFLOW if it did, else I8MM_OK.

@@ -21,7 +21,8 @@ import torch
 from ._lib import I8mmError, WsLayout, check, lib
 
 __all__ = [
-    "I8mmError", "quantize_weight", "linear_forward", "workspace_layout", "workspace_size",
+    "I8mmError", "quantize_weight", "linear_forward", "linear_forward_fp16w", "workspace_layout",
+    "workspace_size",
     "alloc_workspace", "linear_status", "find_outliers", "quantize_rows", "outlier_weights",
     "gemm_s32", "profile_enable", "profile_read", "set_split_override", "Int8Linear",
 ]
@@ -113,6 +114,48 @@ def linear_forward(X: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor,
     return out
 
 
+def linear_forward_fp16w(X: torch.Tensor, W: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                         threshold: float = DEFAULT_THRESHOLD, max_outliers: Optional[int] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None,
+                         CB: Optional[torch.Tensor] = None, SCB: Optional[torch.Tensor] = None):
+    """The layer with the fp16 weight W [N,K] kept: W is quantized on every call
+    (into CB/SCB, allocated when not given) and the outlier weight dims are
+    W[:, O] itself.  Returns (Y, CB, SCB)."""
+    _need(X, "X", torch.float16, 2)
+    _need(W, "W", torch.float16, 2)
+    T, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)} W {tuple(W.shape)}")
+    if bias is not None:
+        _need(bias, "bias", torch.float16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias must have N elements")
+    if CB is None:
+        CB = torch.empty((N, K), dtype=torch.int8, device=X.device)
+    if SCB is None:
+        SCB = torch.empty((N,), dtype=torch.float32, device=X.device)
+    _need(CB, "CB", torch.int8, 2)
+    _need(SCB, "SCB", torch.float32, 1)
+    if tuple(CB.shape) != (N, K) or SCB.shape[0] != N:
+        raise ValueError("CB must be [N, K] and SCB [N]")
+    mo = K if max_outliers is None else max_outliers
+    if workspace is None:
+        workspace = alloc_workspace(T, N, K, mo, X.device)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=X.device)
+    else:
+        _need(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (T, N):
+            raise ValueError("out must be [T, N]")
+    check("int8_linear_forward_fp16w",
+          lib().int8_linear_forward_fp16w(_ptr(X), T, K, _ptr(W), N, _ptr(bias), float(threshold),
+                                          _ptr(CB), _ptr(SCB), _ptr(out), _ptr(workspace),
+                                          workspace.numel(), mo, _stream(X)))
+    return out, CB, SCB
+
+
 def linear_status(workspace: torch.Tensor) -> Tuple[int, int]:
     """(status code, n_outliers) of the last forward call on this workspace (syncs)."""
     n = ctypes.c_int32(0)
@@ -196,23 +239,118 @@ def profile_read():
     return list(ms), int(calls[3])
 
 
-class Int8Linear:
-    """A linear layer holding its weight as CB/SCB (the pages' ``Linear8bitLt``
-    with ``has_fp16_weights=False``): quantize once, then call."""
+class Int8Linear(torch.nn.Module):
+    """``torch.nn.Linear`` in LLM.int8() form: the interface of the pages'
+    ``Linear8bitLt(in_features, out_features, bias, has_fp16_weights,
+    threshold)`` ("transformers への統合" and "accelerate を使ったゼロメモリモデル
+    構築" sections of the Hugging Face summary).
 
-    def __init__(self, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
-                 threshold: float = DEFAULT_THRESHOLD):
-        self.CB, self.SCB = quantize_weight(weight.contiguous())
-        self.bias = None if bias is None else bias.contiguous()
-        self.threshold = threshold
+    Life cycle, as there: build it, load an fp16 ``nn.Linear`` state dict
+    (``weight``, ``bias``), move it to the GPU -- the move quantizes the weight
+    into ``CB`` (int8 [out, in]) and ``SCB`` (fp32 [out]).  With
+    ``has_fp16_weights=False`` the fp16 weight is dropped then; the state dict
+    holds ``CB``, ``SCB`` and ``bias`` and loads back without quantizing again
+    (the int8 form persists).  With ``has_fp16_weights=True`` the fp16 weight
+    stays and every call quantizes it (``linear_forward_fp16w``).  Inputs are
+    fp16 ``[..., in_features]``; the product runs on the GPU only."""
+
+    def __init__(self, in_features: int, out_features: int, bias: bool = True,
+                 has_fp16_weights: bool = False, threshold: float = DEFAULT_THRESHOLD,
+                 device=None):
+        super().__init__()
+        self.in_features = int(in_features)
+        self.out_features = int(out_features)
+        self.has_fp16_weights = bool(has_fp16_weights)
+        self.threshold = float(threshold)
+        self.weight = torch.nn.Parameter(
+            torch.empty((out_features, in_features), dtype=torch.float16, device=device),
+            requires_grad=False)
+        if bias:
+            self.bias = torch.nn.Parameter(
+                torch.zeros(out_features, dtype=torch.float16, device=device), requires_grad=False)
+        else:
+            self.register_parameter("bias", None)
+        # the int8 form (persistent once made); scratch CB/SCB of the fp16 form
+        self.register_buffer("CB", None)
+        self.register_buffer("SCB", None)
         self._ws = None
         self._ws_key = None
+        self._cb_scratch = None
+        self._scb_scratch = None
 
-    def __call__(self, X: torch.Tensor) -> torch.Tensor:
-        T, K = X.shape
+    @classmethod
+    def from_linear(cls, linear: torch.nn.Linear, has_fp16_weights: bool = False,
+                    threshold: float = DEFAULT_THRESHOLD) -> "Int8Linear":
+        m = cls(linear.in_features, linear.out_features, linear.bias is not None,
+                has_fp16_weights, threshold, device=linear.weight.device)
+        m.load_state_dict({k: v.to(torch.float16) for k, v in linear.state_dict().items()})
+        return m
+
+    def extra_repr(self) -> str:
+        return (f"in_features={self.in_features}, out_features={self.out_features}, "
+                f"bias={self.bias is not None}, has_fp16_weights={self.has_fp16_weights}, "
+                f"threshold={self.threshold}, quantized={self.CB is not None}")
+
+    def _quantize_if_on_gpu(self) -> None:
+        w = self.weight
+        if w is None or not w.is_cuda:
+            return
+        if self.has_fp16_weights:
+            return  # quantized on every call
+        self.CB, self.SCB = quantize_weight(w.detach().to(torch.float16).contiguous())
+        self.weight = None  # the int8 form replaces it
+
+    def _apply(self, fn, recurse=True):
+        super()._apply(fn, recurse)
+        self._ws, self._ws_key = None, None
+        self._cb_scratch, self._scb_scratch = None, None
+        self._quantize_if_on_gpu()
+        return self
+
+    def _load_from_state_dict(self, state_dict, prefix, local_metadata, strict, missing_keys,
+                              unexpected_keys, error_msgs):
+        cb, scb = state_dict.get(prefix + "CB"), state_dict.get(prefix + "SCB")
+        if cb is not None and scb is not None:
+            # the int8 form: no fp16 weight to load
+            dev = self.bias.device if self.bias is not None else cb.device
+            self.CB = cb.to(device=dev, dtype=torch.int8).contiguous()
+            self.SCB = scb.to(device=dev, dtype=torch.float32).contiguous()
+            self.weight = None
+            if self.bias is not None and prefix + "bias" in state_dict:
+                with torch.no_grad():
+                    self.bias.copy_(state_dict[prefix + "bias"].to(torch.float16))
+            elif self.bias is not None:
+                missing_keys.append(prefix + "bias")
+            return
+        if self.weight is None and prefix + "weight" in state_dict:
+            self.weight = torch.nn.Parameter(
+                torch.empty((self.out_features, self.in_features), dtype=torch.float16,
+                            device=self.CB.device if self.CB is not None else None),
+                requires_grad=False)
+            self.CB, self.SCB = None, None
+        super()._load_from_state_dict(state_dict, prefix, local_metadata, strict, missing_keys,
+                                      unexpected_keys, error_msgs)
+        self._quantize_if_on_gpu()
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if not x.is_cuda:
+            raise RuntimeError("Int8Linear runs on the GPU only; move the module and the input")
+        lead = x.shape[:-1]
+        X = x.reshape(-1, self.in_features).to(torch.float16).contiguous()
+        T = X.shape[0]
         key = (T, X.device)
         if self._ws_key != key:
-            self._ws = alloc_workspace(T, self.CB.shape[0], K, None, X.device)
+            self._ws = alloc_workspace(T, self.out_features, self.in_features, None, X.device)
             self._ws_key = key
-        return linear_forward(X.contiguous(), self.CB, self.SCB, self.bias, self.threshold,
-                              workspace=self._ws)
+        bias = None if self.bias is None else self.bias.to(torch.float16).contiguous()
+        if self.has_fp16_weights:
+            if self.weight is None or not self.weight.is_cuda:
+                raise RuntimeError("the fp16 weight must be on the GPU")
+            Y, self._cb_scratch, self._scb_scratch = linear_forward_fp16w(
+                X, self.weight.to(torch.float16).contiguous(), bias, self.threshold,
+                workspace=self._ws, CB=self._cb_scratch, SCB=self._scb_scratch)
+        else:
+            if self.CB is None:
+                raise RuntimeError("the weight is not quantized yet; move the module to the GPU")
+            Y = linear_forward(X, self.CB, self.SCB, bias, self.threshold, workspace=self._ws)
+        return Y.reshape(*lead, self.out_features)

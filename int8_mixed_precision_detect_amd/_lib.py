@@ -39,6 +39,8 @@ SIGNATURES = {
     "int8_linear_workspace_size": (c_size, [c_i64, c_i64, c_i64, c_i64]),
     "int8_linear_forward": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_i64, c_ptr, c_float,
                                     c_ptr, c_ptr, c_size, c_i64, c_ptr]),
+    "int8_linear_forward_fp16w": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_i64, c_ptr, c_float,
+                                          c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_i64, c_ptr]),
     "int8_linear_status": (c_int, [c_ptr, ctypes.POINTER(ctypes.c_int32), c_ptr]),
     "int8_find_outliers": (c_int, [c_ptr, c_i64, c_i64, c_float, c_ptr, c_ptr, c_ptr, c_i64,
                                    c_ptr]),

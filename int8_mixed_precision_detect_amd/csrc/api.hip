@@ -109,10 +109,13 @@ size_t int8_linear_workspace_size(int64_t T, int64_t N, int64_t K, int64_t max_o
   return L.total;
 }
 
-i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_t* CB,
-                                const float* SCB, int64_t N, const void* bias, float threshold,
-                                void* Y, void* ws, size_t ws_bytes, int64_t max_outliers,
-                                hipStream_t stream) {
+namespace {
+// The forward.  W16 != null: the fp16-weight variant -- W16 is quantized
+// into CB/SCB first (they are outputs then) and Wo is copied from W16.
+i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, const float* SCB,
+                         int64_t N, const void* bias, float threshold, void* Y, void* ws,
+                         size_t ws_bytes, int64_t max_outliers, hipStream_t stream,
+                         const _Float16* W16) {
   if (isnan(threshold) || !(threshold > 0.0f)) return I8MM_ERR_INVALID_ARG;
   i8mm_ws_layout L;
   const i8mm_status ls = layout_of(T, N, K, max_outliers, &L);
@@ -122,22 +125,27 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   if (bias && !aligned(bias, 2)) return I8MM_ERR_INVALID_ARG;
   if (K > 0 && (!X || !CB || !SCB || !aligned(X, 2) || !aligned(SCB, 4)))
     return I8MM_ERR_INVALID_ARG;
+  if (W16 && K > 0 && !aligned(W16, 2)) return I8MM_ERR_INVALID_ARG;
   if (ws_bytes < L.total) return I8MM_ERR_WORKSPACE;
   (void)hipGetLastError();
 
   char* w = (char*)ws;
   int32_t* counts = (int32_t*)(w + L.counts);
-  if (K == 0) {
-    launch_fill_bias((_Float16*)Y, T, N, (const _Float16*)bias, counts, stream);
-    return hip_status();
-  }
-
   hipEvent_t* ev = nullptr;
-  {
+  if (K > 0) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (g_prof_on && g_prof_n < kProfCap) ev = &g_prof_ev[(size_t)(g_prof_n++) * 4];
   }
   if (ev) (void)hipEventRecord(ev[0], stream);
+  if (W16) {
+    // (in the profile, the per-call weight quantization counts as detection)
+    const bool wvec = (K % 8 == 0) && aligned(W16, 16) && aligned(CB, 8);
+    launch_wquant(W16, N, K, (int8_t*)CB, (float*)SCB, wvec, stream);
+  }
+  if (K == 0) {
+    launch_fill_bias((_Float16*)Y, T, N, (const _Float16*)bias, counts, stream);
+    return hip_status();
+  }
 
   int32_t* O = (int32_t*)(w + L.outliers);
   uint32_t* mask = (uint32_t*)(w + L.mask);
@@ -168,6 +176,7 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   pa.Wo = Wo;
   pa.ocap = max_outliers < kOcap ? max_outliers : kOcap;
   pa.vec = xvec;
+  pa.W16 = W16;
 
   GemmArgs a{};
   a.A = CB;
@@ -194,7 +203,8 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   // aligned operands: the tiled kernel (for few tokens it extracts small
   // outlier weight sets itself); otherwise the generic one
   const bool fast = gemm_i8_supported(a);
-  pa.wo_skip = fast && T <= kFewT ? kFewOcap : -1;
+  a.wo_ready = W16 != nullptr;  // Wo copied from W by step 2, never rebuilt from CB
+  pa.wo_skip = fast && T <= kFewT && !W16 ? kFewOcap : -1;
   launch_prep(pa, stream);
   if (ev) (void)hipEventRecord(ev[2], stream);
 
@@ -202,6 +212,24 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
   if (ge != hipSuccess) return I8MM_ERR_HIP;
   if (ev) (void)hipEventRecord(ev[3], stream);
   return hip_status();
+}
+}  // namespace
+
+i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_t* CB,
+                                const float* SCB, int64_t N, const void* bias, float threshold,
+                                void* Y, void* ws, size_t ws_bytes, int64_t max_outliers,
+                                hipStream_t stream) {
+  return forward_impl(X, T, K, CB, SCB, N, bias, threshold, Y, ws, ws_bytes, max_outliers,
+                      stream, nullptr);
+}
+
+i8mm_status int8_linear_forward_fp16w(const void* X, int64_t T, int64_t K, const void* W,
+                                      int64_t N, const void* bias, float threshold, int8_t* CB,
+                                      float* SCB, void* Y, void* ws, size_t ws_bytes,
+                                      int64_t max_outliers, hipStream_t stream) {
+  if (T > 0 && N > 0 && K > 0 && !W) return I8MM_ERR_INVALID_ARG;
+  return forward_impl(X, T, K, CB, SCB, N, bias, threshold, Y, ws, ws_bytes, max_outliers,
+                      stream, K > 0 ? (const _Float16*)W : nullptr);
 }
 
 i8mm_status int8_linear_status(const void* ws, int32_t* n_outliers, hipStream_t stream) {

@@ -310,7 +310,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     if constexpr (MODE == MODE_FUSED_X) {
       const int64_t n_o = a.counts[0];
       n_use = n_o < a.max_o ? n_o : a.max_o;
-      inloop = n_use <= kFewOcap;
+      inloop = n_use <= kFewOcap && !a.wo_ready;
       if (inloop) {
         for (int64_t o = lane; o < n_use; o += 64) {
           sO[o] = a.O[o];

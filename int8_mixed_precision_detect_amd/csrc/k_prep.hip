@@ -238,13 +238,16 @@ constexpr int kRowChunks = 4;  // 16-byte chunks of a CB row a thread streams (K
 constexpr int kRowsPerPrepBlock = 1;
 
 // RPB rows of X per workgroup, 256 / RPB threads (whole waves) per row
-template <bool VEC, int RPB>
+// F16W: the outlier weights are copied from an fp16 weight W16 [N][K]
+// instead of dequantized from CB (the fp16-weight variant of the layer).
+template <bool VEC, int RPB, bool F16W>
 __global__ __launch_bounds__(256) void k_prep(
     const _Float16* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ mask,
     int32_t* __restrict__ O_out, int32_t* __restrict__ counts, int64_t max_o,
     int8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sx, _Float16* __restrict__ Xo,
     int64_t ldo, int64_t nrowblk, const int8_t* __restrict__ CB, const float* __restrict__ SCB,
-    int64_t N, _Float16* __restrict__ Wo, int64_t ocap, int64_t wo_skip) {
+    int64_t N, _Float16* __restrict__ Wo, int64_t ocap, int64_t wo_skip,
+    const _Float16* __restrict__ W16) {
   // The body uses amdgcn-only types (buffer resources); the host pass only
   // needs the kernel's signature to emit its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(256) void k_prep(
   // Wide outlier sets touch nearly every cache line of a CB row: the channel
   // workgroups then stream whole rows (through the LDS that would hold O)
   // instead of gathering -- see below.
-  const bool wo_stream = !row_block && n_use * 64 >= K && K % 16 == 0 && K + 16 <= ocap * 4 &&
+  const bool wo_stream = !F16W && !row_block && n_use * 64 >= K && K % 16 == 0 && K + 16 <= ocap * 4 &&
                          K <= 256 * kRowChunks * 16 && (((uintptr_t)CB) & 15) == 0;
   if (listed && !wo_stream) outlier_list<256>(smask, spref, KW, n_use, sO);
   if (blockIdx.x == 0 && counts) {
@@ -478,19 +481,34 @@ __global__ __launch_bounds__(256) void k_prep(
       }
       r0 = rr;
       u0 = uu;
-      int8_t c[kGather];
+      if constexpr (F16W) {
+        _Float16 h[kGather];
 #pragma unroll
-      for (int g = 0; g < kGather; ++g) {
-        const int64_t o = ug[g] * 64 + lane;
-        c[g] = (q0 + g < items && o < n_use) ? CB[(j0 + wave + 4 * rg[g]) * K + sO[o]]
-                                             : (int8_t)0;
-      }
+        for (int g = 0; g < kGather; ++g) {
+          const int64_t o = ug[g] * 64 + lane;
+          h[g] = (q0 + g < items && o < n_use) ? W16[(j0 + wave + 4 * rg[g]) * K + sO[o]]
+                                               : (_Float16)0.0f;
+        }
 #pragma unroll
-      for (int g = 0; g < kGather; ++g) {
-        const int64_t o = ug[g] * 64 + lane;
-        if (q0 + g < items && o < n_pad) {
-          const int64_t j = j0 + wave + 4 * rg[g];
-          Wo[j * ldo + o] = dequant_weight(c[g], SCB[j]);
+        for (int g = 0; g < kGather; ++g) {
+          const int64_t o = ug[g] * 64 + lane;
+          if (q0 + g < items && o < n_pad) Wo[(j0 + wave + 4 * rg[g]) * ldo + o] = h[g];
+        }
+      } else {
+        int8_t c[kGather];
+#pragma unroll
+        for (int g = 0; g < kGather; ++g) {
+          const int64_t o = ug[g] * 64 + lane;
+          c[g] = (q0 + g < items && o < n_use) ? CB[(j0 + wave + 4 * rg[g]) * K + sO[o]]
+                                               : (int8_t)0;
+        }
+#pragma unroll
+        for (int g = 0; g < kGather; ++g) {
+          const int64_t o = ug[g] * 64 + lane;
+          if (q0 + g < items && o < n_pad) {
+            const int64_t j = j0 + wave + 4 * rg[g];
+            Wo[j * ldo + o] = dequant_weight(c[g], SCB[j]);
+          }
         }
       }
     }
@@ -507,7 +525,10 @@ __global__ __launch_bounds__(256) void k_prep(
         while (mb && o < n_use) {
           const int b = __ffs(mb) - 1;
           mb &= mb - 1;
-          worow[o++] = dequant_weight(cbrow[w * 32 + b], sj);
+          if constexpr (F16W)
+            worow[o++] = W16[j * K + w * 32 + b];
+          else
+            worow[o++] = dequant_weight(cbrow[w * 32 + b], sj);
         }
       }
       for (int64_t o = n_use + lane; o < n_pad; o += 64) worow[o] = (_Float16)0.0f;
@@ -531,12 +552,18 @@ void launch_prep(const PrepArgs& p, hipStream_t st) {
                               (int)lds);
     kern<<<g, dim3(256), lds, st>>>(p.X, p.T, p.K, p.mask, p.O_out, p.counts, p.max_o, p.Xq,
                                     p.ldq, p.sx, p.Xo, p.ldo, nrowblk, p.CB, p.SCB, p.N, p.Wo,
-                                    p.ocap, p.wo_skip);
+                                    p.ocap, p.wo_skip, p.W16);
   };
-  if (p.vec)
-    go(k_prep<true, kRowsPerPrepBlock>);
-  else
-    go(k_prep<false, kRowsPerPrepBlock>);
+  if (p.W16) {
+    if (p.vec)
+      go(k_prep<true, kRowsPerPrepBlock, true>);
+    else
+      go(k_prep<false, kRowsPerPrepBlock, true>);
+  } else if (p.vec) {
+    go(k_prep<true, kRowsPerPrepBlock, false>);
+  } else {
+    go(k_prep<false, kRowsPerPrepBlock, false>);
+  }
 }
 
 // Y[i, j] = bias[j] (or 0): the layer with K == 0 (no columns, no outliers).

@@ -39,6 +39,8 @@ struct PrepArgs {
   int64_t ocap;     // outlier-list capacity in LDS (entries)
   int64_t wo_skip;  // Wo is built only when the outlier set exceeds this
   bool vec;         // 16-byte aligned rows of X (K % 8 == 0)
+  // fp16 weight [N][K]: Wo copies W16[:, O] instead of dequantizing CB
+  const _Float16* W16 = nullptr;
 };
 size_t prep_lds_bytes(int64_t K, int64_t ocap);
 void launch_prep(const PrepArgs& p, hipStream_t st);
@@ -72,6 +74,9 @@ struct GemmArgs {
   int64_t splits;
   int64_t cfg;  // tile configuration of the plan (see plan_gemm_i8); -1: choose
   int32_t* part;
+  // Wo is already in the workspace (the few-token tiles must not rebuild it
+  // from CB: the fp16-weight variant takes it from W)
+  bool wo_ready;
 };
 
 // Any shape and alignment: register-staged, byte-granular loads.

@@ -58,7 +58,7 @@ import numpy as np
 __all__ = [
     "rhaz", "absmax_codes", "quantize_weight", "find_outliers", "quantize_rows",
     "gather_outliers", "int8_matmul", "outlier_matmul", "aggregate",
-    "linear_forward", "linear_forward_sampled", "error_bound",
+    "linear_forward", "linear_forward_fp16w", "linear_forward_sampled", "error_bound",
 ]
 
 INT8_MAX = 127
@@ -189,6 +189,27 @@ def linear_forward(X, CB, SCB, bias, threshold, return_stages=False):
     Y = aggregate(acc, sx, SCB, P, bias)
     if return_stages:
         return Y, dict(O=O, Xq=Xq, sx=sx, Xo=Xo, Wo=Wo, acc=acc, P=P)
+    return Y
+
+
+def linear_forward_fp16w(X, W, bias, threshold, return_stages=False):
+    """The layer with the fp16 weight kept (``Linear8bitLt`` has a
+    ``has_fp16_weights`` flag; the pages show only its False side).  Reading
+    for the True side: W is quantized on every call exactly as above, and the
+    outlier weight dims are W's own values, Wo = W[:, O] -- the outlier part
+    then multiplies the original fp16 numbers, which is what splitting off the
+    weight dims in 16 bit ("手法" section of the zenn.dev summary) means when
+    the fp16 weight is at hand."""
+    CB, SCB = quantize_weight(W)
+    O = find_outliers(X, threshold)
+    Xq, sx = quantize_rows(X, O)
+    Xo = np.asarray(X)[:, O].astype(np.float16)
+    Wo = np.asarray(W)[:, O].astype(np.float16)
+    acc = int8_matmul(Xq, CB)
+    P = outlier_matmul(Xo, Wo)
+    Y = aggregate(acc, sx, SCB, P, bias)
+    if return_stages:
+        return Y, dict(O=O, Xq=Xq, sx=sx, Xo=Xo, Wo=Wo, acc=acc, P=P, CB=CB, SCB=SCB)
     return Y
 
 

@@ -214,6 +214,56 @@ def test_down_projection_plans_a_split(i8):
     assert lay["splits"] == 2
 
 
+def _fp16w_check(i8, X, W, bias, thr, what):
+    import torch
+    T, K = X.shape
+    N = W.shape[0]
+    say("forward fp16 weight", what, T, K, N, thr)
+    Yo, st = O.linear_forward_fp16w(X, W, bias, thr, return_stages=True)
+    ws = i8.alloc_workspace(T, N, K)
+    Y, CB, SCB = i8.linear_forward_fp16w(dev(X), dev(W), None if bias is None else dev(bias), thr,
+                                         workspace=ws)
+    torch.cuda.synchronize()
+    err = assert_y_close(host(Y), Yo, what)
+    assert np.array_equal(host(CB), st["CB"])
+    assert np.array_equal(host(SCB).view(np.uint32), st["SCB"].view(np.uint32))
+    v = _ws_views(i8, ws, T, N, K, K)
+    n = len(st["O"])
+    assert v["counts"][0] == n
+    assert np.array_equal(v["O"], st["O"].astype(np.int32))
+    assert np.array_equal(v["sx"].view(np.uint32), st["sx"].view(np.uint32))
+    assert np.array_equal(v["Xq"][:, :K], st["Xq"])
+    assert np.array_equal(v["Xo"][:, :n].view(np.uint16), st["Xo"].view(np.uint16))
+    # the outlier weights are W's own fp16 values
+    assert np.array_equal(v["Wo"][:, :n].view(np.uint16), st["Wo"].view(np.uint16))
+    npad = ((n + 31) // 32) * 32
+    assert np.all(v["Wo"][:, n:npad].view(np.uint16) == 0)
+    return Y, err
+
+
+@pytest.mark.parametrize("T,K,N,planted,thr", [
+    (300, 1024, 517, 3, 6.0),     # wide tiles
+    (5, 1040, 70, 40, 6.0),       # few tokens: Wo from W, fp16 tail instead of CB extraction
+    (32, 2048, 1000, 6, 6.0),
+    (17, 12288, 300, 12, 6.0),
+    (16, 2048, 300, 0, 2.5),      # few tokens, more than 128 outlier columns
+    (40, 1000, 130, 5, 6.0),      # K not a multiple of 16: the generic product
+    (64, 256, 96, 0, 1e-6),       # every column an outlier
+])
+def test_fp16_weight_variant(i8, T, K, N, planted, thr):
+    d = make_random_case(T * 5 + K + N + 11, T, K, N, n_planted=planted, bias=True)
+    _fp16w_check(i8, d["X"], d["W"], d["bias"], thr, f"fp16 weight {T}x{K}x{N} thr={thr}")
+
+
+def test_fp16_weight_variant_split_k(i8):
+    d = make_random_case(77, 300, 4112, 700, n_planted=5, bias=True)
+    try:
+        i8.set_split_override(2)
+        _fp16w_check(i8, d["X"], d["W"], d["bias"], 6.0, "fp16 weight, split K x2")
+    finally:
+        i8.set_split_override(0)
+
+
 def test_outlier_overflow_is_reported(i8):
     d = make_random_case(904, 64, 256, 64, n_planted=10)
     say("forward overflow")

@@ -220,10 +220,43 @@ def pin_sampled_matches_full():
     assert np.array_equal(Ys, Y[np.ix_(rows, cols)])
 
 
+def pin_fp16w_all_outliers_is_the_plain_product():
+    """fp16-weight variant, every column an outlier: nothing is quantized on
+    either side, so Y = fp16(X . W^T + b) with the original W -- the textbook
+    product, to within half an fp16 ulp (one final rounding)."""
+    for seed, (T, K, N) in enumerate([(5, 12, 7), (3, 33, 4), (1, 1, 2)]):
+        d = make_random_case(310 + seed, T, K, N)
+        X, W, b = d["X"], d["W"], d["bias"]
+        assert np.all(X != 0)
+        Y, st = O.linear_forward_fp16w(X, W, b, 1e-6, return_stages=True)
+        assert len(st["O"]) == K and np.all(st["Xq"] == 0)
+        ref = _bruteforce_linear(X, W, b)
+        assert np.all(np.abs(Y.astype(np.float64) - ref) <= 0.5 * O.ulp16(Y) + 1e-12)
+
+
+def pin_fp16w_reduces_to_int8_weight_form():
+    """fp16-weight variant: with no outlier the fp16 weight is not used
+    beyond its quantization, so Y equals the int8-weight layer bit for bit;
+    with outliers it differs only through the outlier dims, and stays within
+    the analytic bound of the brute-force product."""
+    d = make_random_case(320, 6, 40, 9, n_planted=3)
+    X, W, b = d["X"], d["W"], d["bias"]
+    CB, SCB = O.quantize_weight(W)
+    assert np.array_equal(O.linear_forward_fp16w(X, W, b, np.inf).view(np.uint16),
+                          O.linear_forward(X, CB, SCB, b, np.inf).view(np.uint16))
+    Y, st = O.linear_forward_fp16w(X, W, b, 6.0, return_stages=True)
+    assert len(st["O"]) == 3
+    assert np.array_equal(st["Wo"].view(np.uint16), W[:, st["O"]].view(np.uint16))
+    ref = _bruteforce_linear(X, W, b)
+    B = O.error_bound(X, W, CB, SCB, st["O"], st["Xq"], st["sx"], Y)
+    assert np.all(np.abs(Y.astype(np.float64) - ref) <= B)
+
+
 PINS = [pin_worked_example, pin_rounding_ties, pin_threshold_tie, pin_detect_bruteforce,
         pin_weight_identity, pin_row_invariants, pin_int_gemm_bruteforce,
         pin_forward_bruteforce, pin_no_outliers_is_plain_vectorwise,
-        pin_all_outliers_is_fp16_product, pin_sampled_matches_full]
+        pin_all_outliers_is_fp16_product, pin_sampled_matches_full,
+        pin_fp16w_all_outliers_is_the_plain_product, pin_fp16w_reduces_to_int8_weight_form]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
