@@ -59,6 +59,7 @@ __all__ = [
     "rhaz", "absmax_codes", "quantize_weight", "find_outliers", "quantize_rows",
     "gather_outliers", "int8_matmul", "outlier_matmul", "aggregate",
     "linear_forward", "linear_forward_fp16w", "linear_forward_sampled", "error_bound",
+    "quantize_rows_zeropoint", "linear_forward_zeropoint", "error_bound_zeropoint",
 ]
 
 INT8_MAX = 127
@@ -136,6 +137,51 @@ def quantize_rows(X: np.ndarray, O: np.ndarray):
     return Xq, sx.astype(np.float32)
 
 
+def quantize_rows_zeropoint(X: np.ndarray, O: np.ndarray):
+    """Zero-point (asymmetric) row quantization of X's kept columns:
+    (Xq int8 [T,K], sx fp32 [T], Z int32 [T]).
+
+    The zenn.dev summary's "Zeropoint Quantization" section: absmax leaves
+    half of [-127, 127] unused for one-signed inputs (ReLU outputs), so the
+    row is min-max normalized with S = 127*2 / (max - min) and an offset Z,
+    X8 = INT8(X*S - Z), X = (X8 + Z) / S.  The offset's own formula is lost
+    on the page; the Hugging Face summary's affine scheme ("Affine
+    Quantization Scheme" section) fixes that zero must map to an integer code.
+    Reading, per row over the columns not in O:
+      a = min(0, min x), b = max(0, max x)    (the range holds 0)
+      d = fl32(b - a); S = fl32(254 / d); Z = rhaz(fl32(a * S)) + 127
+      code = clamp(rhaz(fl32(fl32(x * S) - Z)), -127, 127), 0 on O
+      sx = fl32(d / 2), so that x ~= (code + Z) * sx / 127
+    A row with b == a (all kept values 0, or none kept) gets S = Z = sx = 0
+    and codes 0.  Zero maps to the code -Z exactly.
+    """
+    X = np.asarray(X)
+    T, K = X.shape
+    keep = np.ones(K, dtype=bool)
+    keep[np.asarray(O, dtype=np.int64)] = False
+    x32 = X.astype(np.float32)
+    Xq = np.zeros((T, K), dtype=np.int8)
+    sx = np.zeros(T, dtype=np.float32)
+    Z = np.zeros(T, dtype=np.int32)
+    for i in range(T):
+        v = x32[i, keep]
+        a = np.float32(min(0.0, float(v.min()))) if v.size else np.float32(0)
+        b = np.float32(max(0.0, float(v.max()))) if v.size else np.float32(0)
+        if b == a:
+            continue
+        d = np.float32(b - a)
+        S = np.float32(np.float32(2 * INT8_MAX) / d)
+        z = int(rhaz(np.float32(a * S))) + INT8_MAX
+        t = (x32[i] * S).astype(np.float32)
+        t = (t - np.float32(z)).astype(np.float32)
+        q = np.clip(rhaz(t), -INT8_MAX, INT8_MAX)
+        q = np.where(keep, q, 0.0)
+        Xq[i] = q.astype(np.int8)
+        sx[i] = np.float32(d / np.float32(2))
+        Z[i] = z
+    return Xq, sx, Z
+
+
 def gather_outliers(X: np.ndarray, CB: np.ndarray, SCB: np.ndarray, O: np.ndarray):
     """Step (2), outlier side: Xo = X[:, O] (fp16) and the matching weight dims.
 
@@ -211,6 +257,50 @@ def linear_forward_fp16w(X, W, bias, threshold, return_stages=False):
     if return_stages:
         return Y, dict(O=O, Xq=Xq, sx=sx, Xo=Xo, Wo=Wo, acc=acc, P=P, CB=CB, SCB=SCB)
     return Y
+
+
+def linear_forward_zeropoint(X, CB, SCB, bias, threshold, return_stages=False):
+    """The layer with zero-point activation quantization (see
+    ``quantize_rows_zeropoint``); the weight side is unchanged.  Since
+    x ~= (q + Z) sx / 127 on the kept columns, the int8 part is
+    (sx s / 127^2) (sum_k q c + Z R_j), with R_j = sum of CB[j, k] over the
+    kept columns -- an exact integer correction, then the same dequantize and
+    aggregate step."""
+    O = find_outliers(X, threshold)
+    Xq, sx, Z = quantize_rows_zeropoint(X, O)
+    Xo, Wo = gather_outliers(X, CB, SCB, O)
+    K = X.shape[1]
+    keep = np.ones(K, dtype=bool)
+    keep[O] = False
+    R = (CB.astype(np.int64) * keep[None, :]).sum(axis=1)
+    acc = int8_matmul(Xq, CB) + Z.astype(np.int64)[:, None] * R[None, :]
+    P = outlier_matmul(Xo, Wo)
+    Y = aggregate(acc, sx, SCB, P, bias)
+    if return_stages:
+        return Y, dict(O=O, Xq=Xq, sx=sx, Z=Z, R=R, Xo=Xo, Wo=Wo, acc=acc, P=P)
+    return Y
+
+
+def error_bound_zeropoint(X, W, CB, SCB, O, Xq, sx, Z, Y):
+    """``error_bound`` for the zero-point layer: a kept activation is
+    x = (sx/127)(q + Z + d) with |d| <= 1/2 plus the fp32 roundings of x*S,
+    of S and of sx (relative 2^-22 of |q + Z| at most), so |q| becomes
+    |q + Z| in the int8 term."""
+    T, K = X.shape
+    keep = np.ones(K, dtype=bool)
+    keep[np.asarray(O, dtype=np.int64)] = False
+    qz = np.abs(Xq.astype(np.float64) + Z.astype(np.float64)[:, None]) * keep[None, :]
+    c = np.abs(CB.astype(np.float64))
+    nk = keep.sum()
+    csum = (c * keep[None, :]).sum(1)[None, :]
+    term_int = 0.5 * qz.sum(1)[:, None] + 0.5 * csum + 0.25 * nk
+    term_int = term_int + (2.0 ** -15) * (qz.sum(1)[:, None] + csum + nk)
+    scale = sx.astype(np.float64)[:, None] * SCB.astype(np.float64)[None, :] / 127.0 ** 2
+    ax = np.abs(X.astype(np.float64))
+    xo = (ax * (~keep)[None, :]).sum(1)
+    term_out = xo[:, None] * (SCB.astype(np.float64)[None, :] * (1.0 / 254 + 2.0 ** -10))
+    slack = 1e-6 * (ax @ np.abs(W.astype(np.float64)).T)
+    return scale * term_int + term_out + 0.5 * ulp16(Y) + slack
 
 
 def linear_forward_sampled(X, CB_rows, SCB_rows, bias_rows, threshold, rows, O=None):

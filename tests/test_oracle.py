@@ -252,11 +252,88 @@ def pin_fp16w_reduces_to_int8_weight_form():
     assert np.all(np.abs(Y.astype(np.float64) - ref) <= B)
 
 
+def pin_zeropoint_relu_row_uses_the_full_range():
+    """The zenn.dev summary's "Zeropoint Quantization" motivation: a
+    one-signed (post-ReLU) row uses only half of the codes under absmax but
+    all of [-127, 127] under zero-point; zero maps to the integer code -Z
+    (the affine scheme's zero point); the scale and offset follow the page's
+    S = 127*2 / (max - min)."""
+    x = np.array([[0.0, 0.5, 1.2, 5.4, 2.0, 0.0, 3.3, 0.25]], dtype=np.float16)
+    q_abs, _ = O.quantize_rows(x, np.array([], dtype=np.int64))
+    assert q_abs.min() >= 0 and q_abs.max() == 127
+    q, sx, Z = O.quantize_rows_zeropoint(x, np.array([], dtype=np.int64))
+    assert q.min() == -127 and q.max() == 127
+    b = float(np.float16(5.4))
+    S = np.float32(254) / np.float32(b)
+    assert Z[0] == 127                       # a = 0: zero is the lowest code
+    assert np.all(q[0][x[0] == 0] == -Z[0])
+    assert sx[0] == np.float32(np.float32(b) / 2)
+    # codes by hand for two values: x*S - Z, rounded half away from zero
+    assert q[0, 2] == int(np.trunc(float(np.float32(np.float32(np.float16(1.2)) * S)) - 127 - 0.5))
+    assert q[0, 4] == int(np.trunc(float(np.float32(np.float32(2.0) * S)) - 127 - 0.5))  # -32.9
+    # a two-signed row with min = -max: the offset is 0, as for absmax
+    q2, sx2, Z2 = O.quantize_rows_zeropoint(np.array([[-2.0, 1.0, 2.0, 0.5]], np.float16),
+                                            np.array([], dtype=np.int64))
+    assert Z2[0] == 0 and sx2[0] == np.float32(2.0) and q2[0, 0] == -127 and q2[0, 2] == 127
+
+
+def pin_zeropoint_roundtrip_and_zero_rows():
+    """Every kept x is within half a step of (q + Z) sx / 127 (plus fp32
+    roundings); outlier columns get code 0; an all-zero row gets S = Z = 0."""
+    d = make_random_case(330, 7, 50, 3, n_planted=2, row_frac=0.5)
+    X = d["X"].copy()
+    X[2] = np.abs(X[2])          # one-signed rows
+    X[3] = -np.abs(X[3])
+    X[4] = 0                     # all zero
+    Oo = O.find_outliers(X, 6.0)
+    q, sx, Z = O.quantize_rows_zeropoint(X, Oo)
+    keep = np.ones(X.shape[1], bool)
+    keep[Oo] = False
+    assert np.all(q[:, Oo] == 0)
+    assert sx[4] == 0 and Z[4] == 0 and np.all(q[4] == 0)
+    xh = (q.astype(np.float64) + Z[:, None]) * sx.astype(np.float64)[:, None] / 127
+    err = np.abs(xh - X.astype(np.float64))[:, keep]
+    step = sx.astype(np.float64)[:, None] / 127
+    assert np.all(err <= 0.5 * step * (1 + 2.0 ** -12) + 1e-12)
+    assert np.all(np.abs(Z) <= 127)
+
+
+def _bound_check_zeropoint(X, W, b, thr):
+    CB, SCB = O.quantize_weight(W)
+    Y, st = O.linear_forward_zeropoint(X, CB, SCB, b, thr, return_stages=True)
+    ref = _bruteforce_linear(X, W, b)
+    B = O.error_bound_zeropoint(X, W, CB, SCB, st["O"], st["Xq"], st["sx"], st["Z"], Y)
+    err = np.abs(Y.astype(np.float64) - ref)
+    assert np.all(err <= B), float((err - B).max())
+    return Y, st
+
+
+def pin_zeropoint_forward_bruteforce():
+    """The zero-point layer against the brute-force float64 X.W^T + b (with
+    the original W), within its analytic bound, on two-signed, one-signed and
+    zero rows, with and without outliers."""
+    shapes = [(1, 1, 1), (1, 7, 3), (3, 5, 2), (4, 9, 11), (2, 33, 5), (5, 16, 8)]
+    for s_, (T, K, N) in enumerate(shapes):
+        for planted in (0, 2):
+            d = make_random_case(340 + s_, T, K, N, n_planted=min(planted, K), bias=(s_ % 2 == 0))
+            X = d["X"].copy()
+            X[0] = np.abs(X[0])
+            _bound_check_zeropoint(X, d["W"], d["bias"], d["threshold"])
+    # the int8 product alone would be off by sx*s/127^2 * Z*R: the bound
+    # holds only with the correction
+    d = make_random_case(350, 4, 64, 6)
+    X = np.abs(d["X"])
+    Y, st = _bound_check_zeropoint(X, d["W"], d["bias"], np.inf)
+    assert np.all(st["Z"] == 127)
+
+
 PINS = [pin_worked_example, pin_rounding_ties, pin_threshold_tie, pin_detect_bruteforce,
         pin_weight_identity, pin_row_invariants, pin_int_gemm_bruteforce,
         pin_forward_bruteforce, pin_no_outliers_is_plain_vectorwise,
         pin_all_outliers_is_fp16_product, pin_sampled_matches_full,
-        pin_fp16w_all_outliers_is_the_plain_product, pin_fp16w_reduces_to_int8_weight_form]
+        pin_fp16w_all_outliers_is_the_plain_product, pin_fp16w_reduces_to_int8_weight_form,
+        pin_zeropoint_relu_row_uses_the_full_range, pin_zeropoint_roundtrip_and_zero_rows,
+        pin_zeropoint_forward_bruteforce]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
