@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define I8MM_ABI_VERSION 3
+#define I8MM_ABI_VERSION 4
 
 typedef enum {
   I8MM_OK = 0,
@@ -102,10 +102,14 @@ typedef struct {
   size_t counts;   /* int32[4]: n_o (true count), overflow flag, 0, 0          */
   size_t outliers; /* int32[max_outliers]: outlier columns O, ascending       */
   size_t mask;     /* uint32[ceil(K/32)]: bit k set iff column k is an outlier */
-  size_t sx;       /* fp32[T]: row scales (absmax over non-outlier columns)    */
+  size_t sx;       /* fp32[T]: row scales (absmax over non-outlier columns;    */
+                   /* zero-point layer: half their range, see below)           */
   size_t xq;       /* int8[T][ldq]: quantized X, outlier and pad columns 0     */
   size_t xo;       /* fp16[T][ldo]: X[:, O], zero-padded to ldo                */
   size_t wo;       /* fp16[N][ldo]: fp16(CB[:, O] * SCB / 127), zero-padded    */
+  size_t zp;       /* int32[T]: zero-point offsets Z of the rows (zero-point   */
+                   /* layer only)                                              */
+  size_t osum;     /* int32[N]: sum_o CB[j, O_o] (zero-point layer, n_o > 0)   */
   size_t part;     /* int32 partial accumulators of a K-split product: one    */
                    /* tile of the product per split (0 bytes when splits == 1) */
   int64_t ldq;     /* row pitch of xq in bytes (K rounded up to 64)            */
@@ -179,6 +183,35 @@ i8mm_status int8_linear_forward_fp16w(const void* X, int64_t T, int64_t K, const
                                       int64_t N, const void* bias, float threshold, int8_t* CB,
                                       float* SCB, void* Y, void* ws, size_t ws_bytes,
                                       int64_t max_outliers, hipStream_t stream);
+
+/*
+ * Zero-point (asymmetric) activation quantization ("Zeropoint Quantization"
+ * section of the zenn.dev LLM.int8() summary: S = 127*2 / (max - min),
+ * X8 = INT8(X*S - Z); zero is an integer code as in the Hugging Face
+ * summary's affine scheme).  Per row i over the columns not in O:
+ *
+ *   a = min(0, min x), b = max(0, max x), d = fl32(b - a)
+ *   S = fl32(254 / d), Z[i] = rhaz(fl32(a * S)) + 127
+ *   Xq = clamp(rhaz(fl32(fl32(x * S) - Z)), -127, 127), 0 on O
+ *   sx[i] = d / 2                       (x ~= (Xq + Z) * sx / 127)
+ *   (b == a: S = Z = sx = 0, codes 0)
+ *   Y[i,j] = fp16( (acc + Z[i] * R[j]) * sx[i] * SCB[j] / 127^2
+ *                  + sum_o X[i,O_o] * Wo[j,o] + bias[j] )
+ *   with R[j] = sum over the columns not in O of CB[j, k]
+ *
+ * The weight side is unchanged (int8_quantize_weight).  rsum = CB's row sums
+ * over all K, int32 [N], from int8_weight_rowsum (once per weight).  The
+ * offset term is added in fp32 (as the product of a per-row and a
+ * per-channel factor); everything else, the workspace (zp and osum regions)
+ * and the errors are as int8_linear_forward.
+ */
+i8mm_status int8_weight_rowsum(const int8_t* CB, int64_t N, int64_t K, int32_t* rsum,
+                               hipStream_t stream);
+i8mm_status int8_linear_forward_zeropoint(const void* X, int64_t T, int64_t K, const int8_t* CB,
+                                          const float* SCB, const int32_t* rsum, int64_t N,
+                                          const void* bias, float threshold, void* Y, void* ws,
+                                          size_t ws_bytes, int64_t max_outliers,
+                                          hipStream_t stream);
 
 /*
  * Synchronizes `stream`, then reads the counts of the last forward call that

@@ -21,7 +21,8 @@ import torch
 from ._lib import I8mmError, WsLayout, check, lib
 
 __all__ = [
-    "I8mmError", "quantize_weight", "linear_forward", "linear_forward_fp16w", "workspace_layout",
+    "I8mmError", "quantize_weight", "linear_forward", "linear_forward_fp16w", "weight_rowsum",
+    "linear_forward_zeropoint", "workspace_layout",
     "workspace_size",
     "alloc_workspace", "linear_status", "find_outliers", "quantize_rows", "outlier_weights",
     "gemm_s32", "profile_enable", "profile_read", "set_split_override", "Int8Linear",
@@ -154,6 +155,51 @@ def linear_forward_fp16w(X: torch.Tensor, W: torch.Tensor, bias: Optional[torch.
                                           _ptr(CB), _ptr(SCB), _ptr(out), _ptr(workspace),
                                           workspace.numel(), mo, _stream(X)))
     return out, CB, SCB
+
+
+def weight_rowsum(CB: torch.Tensor) -> torch.Tensor:
+    """int32 [N] row sums of CB (once per weight, for the zero-point layer)."""
+    _need(CB, "CB", torch.int8, 2)
+    N, K = CB.shape
+    out = torch.empty((N,), dtype=torch.int32, device=CB.device)
+    check("int8_weight_rowsum", lib().int8_weight_rowsum(_ptr(CB), N, K, _ptr(out), _stream(CB)))
+    return out
+
+
+def linear_forward_zeropoint(X: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor,
+                             rsum: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                             threshold: float = DEFAULT_THRESHOLD,
+                             max_outliers: Optional[int] = None,
+                             workspace: Optional[torch.Tensor] = None,
+                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer with zero-point (asymmetric) row quantization of X; rsum from
+    ``weight_rowsum(CB)``."""
+    _need(X, "X", torch.float16, 2)
+    _need(CB, "CB", torch.int8, 2)
+    _need(SCB, "SCB", torch.float32, 1)
+    _need(rsum, "rsum", torch.int32, 1)
+    T, K = X.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or SCB.shape[0] != N or rsum.shape[0] != N:
+        raise ValueError("shape mismatch")
+    if bias is not None:
+        _need(bias, "bias", torch.float16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias must have N elements")
+    mo = K if max_outliers is None else max_outliers
+    if workspace is None:
+        workspace = alloc_workspace(T, N, K, mo, X.device)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=X.device)
+    else:
+        _need(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (T, N):
+            raise ValueError("out must be [T, N]")
+    check("int8_linear_forward_zeropoint",
+          lib().int8_linear_forward_zeropoint(_ptr(X), T, K, _ptr(CB), _ptr(SCB), _ptr(rsum), N,
+                                              _ptr(bias), float(threshold), _ptr(out),
+                                              _ptr(workspace), workspace.numel(), mo, _stream(X)))
+    return out
 
 
 def linear_status(workspace: torch.Tensor) -> Tuple[int, int]:

@@ -24,7 +24,8 @@ c_float = ctypes.c_float
 class WsLayout(ctypes.Structure):
     _fields_ = [
         ("counts", c_size), ("outliers", c_size), ("mask", c_size), ("sx", c_size),
-        ("xq", c_size), ("xo", c_size), ("wo", c_size), ("part", c_size),
+        ("xq", c_size), ("xo", c_size), ("wo", c_size), ("zp", c_size), ("osum", c_size),
+        ("part", c_size),
         ("ldq", c_i64), ("ldo", c_i64), ("splits", c_i64), ("total", c_size),
     ]
 
@@ -39,6 +40,9 @@ SIGNATURES = {
     "int8_linear_workspace_size": (c_size, [c_i64, c_i64, c_i64, c_i64]),
     "int8_linear_forward": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_i64, c_ptr, c_float,
                                     c_ptr, c_ptr, c_size, c_i64, c_ptr]),
+    "int8_weight_rowsum": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr]),
+    "int8_linear_forward_zeropoint": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_ptr, c_i64,
+                                              c_ptr, c_float, c_ptr, c_ptr, c_size, c_i64, c_ptr]),
     "int8_linear_forward_fp16w": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_i64, c_ptr, c_float,
                                           c_ptr, c_ptr, c_ptr, c_ptr, c_size, c_i64, c_ptr]),
     "int8_linear_status": (c_int, [c_ptr, ctypes.POINTER(ctypes.c_int32), c_ptr]),

@@ -42,8 +42,13 @@ i8mm_status layout_of(int64_t T, int64_t N, int64_t K, int64_t max_o, i8mm_ws_la
   L->xq = take((size_t)T * (size_t)L->ldq);
   L->xo = take((size_t)T * (size_t)L->ldo * 2);
   L->wo = take((size_t)N * (size_t)L->ldo * 2);
+  L->zp = take((size_t)(T > 0 ? T : 1) * 4);
+  L->osum = take((size_t)(N > 0 ? N : 1) * 4);
+  // partial tiles: room for the plans of both layers (the zero-point one
+  // runs only the 256-channel tiles)
   const GemmPlan gp = plan_gemm_i8(T, N, K);
-  L->part = take((size_t)gp.part_elems * 4);
+  const GemmPlan gz = plan_gemm_i8(T, N, K, true);
+  L->part = take((size_t)(gp.part_elems > gz.part_elems ? gp.part_elems : gz.part_elems) * 4);
   L->splits = gp.splits;
   L->total = off;
   return I8MM_OK;
@@ -112,10 +117,11 @@ size_t int8_linear_workspace_size(int64_t T, int64_t N, int64_t K, int64_t max_o
 namespace {
 // The forward.  W16 != null: the fp16-weight variant -- W16 is quantized
 // into CB/SCB first (they are outputs then) and Wo is copied from W16.
+// rsum != null: the zero-point layer (rsum = CB's row sums).
 i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, const float* SCB,
                          int64_t N, const void* bias, float threshold, void* Y, void* ws,
                          size_t ws_bytes, int64_t max_outliers, hipStream_t stream,
-                         const _Float16* W16) {
+                         const _Float16* W16, const int32_t* rsum = nullptr) {
   if (isnan(threshold) || !(threshold > 0.0f)) return I8MM_ERR_INVALID_ARG;
   i8mm_ws_layout L;
   const i8mm_status ls = layout_of(T, N, K, max_outliers, &L);
@@ -177,6 +183,12 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   pa.ocap = max_outliers < kOcap ? max_outliers : kOcap;
   pa.vec = xvec;
   pa.W16 = W16;
+  int32_t* zp = (int32_t*)(w + L.zp);
+  int32_t* osum = (int32_t*)(w + L.osum);
+  if (rsum) {
+    pa.zp = zp;
+    pa.osum = osum;
+  }
 
   GemmArgs a{};
   a.A = CB;
@@ -196,15 +208,22 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   a.max_o = max_outliers;
   a.bias = (const _Float16*)bias;
   a.Y = (_Float16*)Y;
-  const GemmPlan gp = plan_gemm_i8(T, N, K);
+  const GemmPlan gp = plan_gemm_i8(T, N, K, rsum != nullptr);
   a.cfg = gp.cfg;
   a.splits = gp.splits;
   a.part = gp.part_elems > 0 ? (int32_t*)(w + L.part) : nullptr;
+  if (rsum) {
+    a.zp = zp;
+    a.rsum = rsum;
+    a.osum = osum;
+  }
   // aligned operands: the tiled kernel (for few tokens it extracts small
   // outlier weight sets itself); otherwise the generic one
   const bool fast = gemm_i8_supported(a);
-  a.wo_ready = W16 != nullptr;  // Wo copied from W by step 2, never rebuilt from CB
-  pa.wo_skip = fast && T <= kFewT && !W16 ? kFewOcap : -1;
+  // Wo (and, zero-point, the outlier code sums) built by step 2: the
+  // few-token tiles then do not rebuild Wo from CB
+  a.wo_ready = W16 != nullptr || rsum != nullptr;
+  pa.wo_skip = fast && T <= kFewT && !a.wo_ready ? kFewOcap : -1;
   launch_prep(pa, stream);
   if (ev) (void)hipEventRecord(ev[2], stream);
 
@@ -221,6 +240,27 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
                                 hipStream_t stream) {
   return forward_impl(X, T, K, CB, SCB, N, bias, threshold, Y, ws, ws_bytes, max_outliers,
                       stream, nullptr);
+}
+
+i8mm_status int8_weight_rowsum(const int8_t* CB, int64_t N, int64_t K, int32_t* rsum,
+                               hipStream_t stream) {
+  if (N < 0 || K < 0) return I8MM_ERR_INVALID_ARG;
+  if (N == 0) return I8MM_OK;
+  if (!rsum || !aligned(rsum, 4) || (K > 0 && !CB)) return I8MM_ERR_INVALID_ARG;
+  if (N >= kMaxDim || K >= kMaxDim) return I8MM_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  launch_rowsum(CB, N, K, rsum, stream);
+  return hip_status();
+}
+
+i8mm_status int8_linear_forward_zeropoint(const void* X, int64_t T, int64_t K, const int8_t* CB,
+                                          const float* SCB, const int32_t* rsum, int64_t N,
+                                          const void* bias, float threshold, void* Y, void* ws,
+                                          size_t ws_bytes, int64_t max_outliers,
+                                          hipStream_t stream) {
+  if (T > 0 && N > 0 && K > 0 && (!rsum || !aligned(rsum, 4))) return I8MM_ERR_INVALID_ARG;
+  return forward_impl(X, T, K, CB, SCB, N, bias, threshold, Y, ws, ws_bytes, max_outliers, stream,
+                      nullptr, K > 0 ? rsum : nullptr);
 }
 
 i8mm_status int8_linear_forward_fp16w(const void* X, int64_t T, int64_t K, const void* W,

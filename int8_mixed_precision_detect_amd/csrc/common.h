@@ -96,6 +96,80 @@ __device__ __forceinline__ _Float16 dequant_weight(int c, float s) {
   return (_Float16)div_by(p, 127.0f, 1.0f / 127.0f);
 }
 
+// ---- zero-point (asymmetric) row codes ----
+// Round half away from zero, exactly: v - trunc(v) is exact in fp32.
+__device__ __forceinline__ float rhaz_exact(float v) {
+  const float t = __builtin_truncf(v);
+  return __builtin_fabsf(v - t) >= 0.5f ? t + __builtin_copysignf(1.0f, v) : t;
+}
+
+// Parameters of a row whose kept values span [lo, hi] with lo <= 0 <= hi:
+// d = fl32(hi - lo), S = fl32(254 / d), Z = rhaz(fl32(lo * S)) + 127 and
+// sx = d / 2 (exact); a row with hi == lo gets S = Z = sx = 0.
+struct ZpRow {
+  float S, sx;
+  int Z;
+};
+__device__ __forceinline__ ZpRow zp_row(float lo, float hi) {
+#pragma clang fp contract(off)
+  ZpRow z{0.0f, 0.0f, 0};
+  const float d = hi - lo;
+  if (d > 0.0f) {
+    z.S = __fdiv_rn(254.0f, d);  // correctly rounded
+    z.Z = (int)rhaz_exact(lo * z.S) + 127;
+    z.sx = d * 0.5f;
+  }
+  return z;
+}
+
+// Zero-point code of a kept value: clamp(rhaz(fl32(fl32(x * S) - Z)), +-127)
+// (contraction off: the product is rounded before the subtraction, as the
+// definition says, not fused into one multiply-add)
+__device__ __forceinline__ int zp_code(float x, const ZpRow& z) {
+#pragma clang fp contract(off)
+  const float p = x * z.S;  // written out here: the pragma covers only these
+  const float t = p - (float)z.Z;
+  const float q = rhaz_exact(t);
+  return (int)__builtin_fminf(127.0f, __builtin_fmaxf(-127.0f, q));
+}
+
+// Codes of 8 fp16 values; positions whose bit is set in the low 8 bits of
+// `bits` (outlier columns) get code 0.
+__device__ __forceinline__ v2u zp_codes8(v8h v, uint32_t bits, const ZpRow& z) {
+  v2u out;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int e = 4 * w + b;
+      const int q = ((bits >> e) & 1u) ? 0 : zp_code((float)v[e], z);
+      word |= ((uint32_t)q & 0xffu) << (8 * b);
+    }
+    out[w] = word;
+  }
+  return out;
+}
+
+// min and max of 8 fp16 values (exact), as floats
+__device__ __forceinline__ void minmax8(v8h v, float& lo, float& hi) {
+  typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+  v2h mn = v2h{v[0], v[1]}, mx = mn;
+#pragma unroll
+  for (int e = 2; e < 8; e += 2) {
+    mn = __builtin_elementwise_min(mn, v2h{v[e], v[e + 1]});
+    mx = __builtin_elementwise_max(mx, v2h{v[e], v[e + 1]});
+  }
+  lo = fminf(lo, fminf((float)mn[0], (float)mn[1]));
+  hi = fmaxf(hi, fmaxf((float)mx[0], (float)mx[1]));
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

@@ -227,13 +227,28 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(GemmArgs a)
     }
 
     // ---- bias, fp16 round-to-nearest-even, store ----
+    // (zero-point activations: plus the offset part of the int8 product,
+    // (sx Z / 127) (SCB (rsum - osum) / 127), a rank-1 fp32 term)
     const bool yvec = ((a.N & 3) == 0) && ((((uintptr_t)a.Y) & 7) == 0);
+    float ut[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int64_t t = n0 + wn0 + j * 16 + lcol;
+      ut[j] = (a.zp && t < a.T) ? a.sx[t] * (float)a.zp[t] * (1.0f / 127.0f) : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int64_t f = m0 + wm0 + i * 16 + lrow;
       float bv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) bv[r] = (a.bias && f + r < a.N) ? h2f(a.bias[f + r]) : 0.0f;
+      float vr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vr[r] = (a.zp && f + r < a.N)
+                    ? a.SCB[f + r] * (float)(a.rsum[f + r] - (nt > 0 ? a.osum[f + r] : 0)) *
+                          (1.0f / 127.0f)
+                    : 0.0f;
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int64_t t = n0 + wn0 + j * 16 + lcol;
@@ -242,7 +257,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(GemmArgs a)
         const v4f v = __builtin_bit_cast(v4f, acc[i][j]);
         v4h y;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = (_Float16)(v[r] + bv[r]);
+        for (int r = 0; r < 4; ++r)
+          y[r] = (_Float16)(a.zp ? v[r] + bv[r] + ut[j] * vr[r] : v[r] + bv[r]);
         if (yvec && f + 3 < a.N) {
           *(v4h*)dst = y;
         } else {

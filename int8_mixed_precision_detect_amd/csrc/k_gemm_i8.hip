@@ -91,7 +91,9 @@ __device__ __forceinline__ void wait_lgkm0() {
 
 // NTA: the weight operand's slice loads are non-temporal (streamed once: the
 // few-token shapes, where each weight byte is used by one workgroup).
-template <int BM, int BN, int WM, int WN, int S, int KB, int MODE, bool NTA>
+// ZP: zero-point activations -- the epilogue adds the offset part of the
+// int8 product, (sx Z / 127)(SCB (rsum - osum) / 127), before the store.
+template <int BM, int BN, int WM, int WN, int S, int KB, int MODE, bool NTA, bool ZP>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs a) {
   // The body uses amdgcn-only types (buffer resources); the host pass only
   // needs the kernel's signature to emit its launch stub.
@@ -522,9 +524,36 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       run(F16Slices{}, 0, Kt, [] {}, tail_buf, tail_pre ? 1 : 0);
     }
     const bool yvec = ((a.N & 3) == 0) && ((((uintptr_t)a.Y) & 7) == 0);
+    // Zero-point activations: the offset part of the int8 product,
+    // (sx Z / 127) (SCB R / 127) with R the channel's kept-column code sum,
+    // is a rank-1 term; it is added here in fp32, one factor per token and
+    // one per channel, rather than to the int32 accumulators (where its
+    // extra registers would not fit the widest tile).
+    float ut[ZP ? NI : 1];
+    if constexpr (ZP) {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const int64_t t = n0 + wn0 + j * 16 + lcol;
+        const int64_t tc = t < a.T ? t : a.T - 1;
+        const float sxt = a.sx[tc];
+        const int z = a.zp[tc];
+        ut[j] = t < a.T ? sxt * (float)z * (1.0f / 127.0f) : 0.0f;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int64_t f = m0 + wm0 + i * 16 + lrow;  // 4 consecutive channels
+      float vr[ZP ? 4 : 1];
+      if constexpr (ZP) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t fc = f + r < a.N ? f + r : a.N - 1;
+          const int rs = a.rsum[fc];
+          const int os = Kt > 0 ? a.osum[fc] : 0;
+          const float sv = a.SCB[fc];
+          vr[r] = f + r < a.N ? sv * (float)(rs - os) * (1.0f / 127.0f) : 0.0f;
+        }
+      }
       float bv[4];
       if constexpr (MODE == MODE_FUSED_X) {
         // short kernels: clamped, unconditional loads, all four in flight
@@ -550,7 +579,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
         const v4f v = __builtin_bit_cast(v4f, acc[i][j]);
         v4h y;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = (_Float16)(v[r] + bv[r]);
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (ZP)
+            y[r] = (_Float16)(v[r] + bv[r] + ut[j] * vr[r]);
+          else
+            y[r] = (_Float16)(v[r] + bv[r]);
+        }
         _Float16* dst = a.Y + t * a.N + f;
         if (yvec && f + 3 < a.N) {
           *(v4h*)dst = y;
@@ -566,11 +600,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
 }
 
 namespace {
-template <int BM, int BN, int WM, int WN, int S, int KB, int MODE, bool NTA = false>
+template <int BM, int BN, int WM, int WN, int S, int KB, int MODE, bool NTA = false,
+          bool ZP = false>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
   constexpr size_t LDS = (size_t)S * (BM + BN) * KB + (MODE == MODE_FUSED_X ? few_lds(BN) : 0);
-  auto kern = k_gemm_i8<BM, BN, WM, WN, S, KB, MODE, NTA>;
+  auto kern = k_gemm_i8<BM, BN, WM, WN, S, KB, MODE, NTA, ZP>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
   if (e != hipSuccess) return e;
@@ -607,8 +642,8 @@ constexpr int64_t kMinSplitK = 1024;  // bytes of K a split walks at least
 // in two full waves (configuration 1 would need 640 tiles, 2.5 waves); the
 // 13B down projection (5120 x 2048 outputs, K = 20480) has only 128 tiles,
 // so K is split in two: 256 workgroups, one full wave.
-void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split, int64_t* cfg,
-                 int64_t* splits) {
+void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split, bool only_cfg1,
+                 int64_t* cfg, int64_t* splits) {
   const int64_t cus = cu_count();
   const int64_t slices = ceil_div(K, 128) > 0 ? ceil_div(K, 128) : 1;
   const int64_t ovr = allow_split ? g_split_override.load() : 1;
@@ -622,7 +657,7 @@ void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split, int64_t* cfg
   for (int64_t sp = 1; sp <= kMaxSplits; ++sp) {
     if (ovr > 0 && sp != want) continue;
     if (ovr == 0 && sp > 1 && (ceil_div(K, sp) < kMinSplitK || sp > slices)) continue;
-    for (int c = 1; c >= 0; --c) {
+    for (int c = 1; c >= (only_cfg1 ? 1 : 0); --c) {
       const int64_t tiles = ceil_div(N, kCfgBM[c]) * ceil_div(T, kCfgBN[c]);
       const double cost = (double)ceil_div(tiles * sp, cus) * (double)(kCfgBM[c] * kCfgBN[c]) *
                           (double)ceil_div(slices, sp) * (sp > 1 ? 1.05 : 1.0);
@@ -636,46 +671,62 @@ void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split, int64_t* cfg
   }
 }
 
-template <int MODE>
-hipError_t launch_mode(const GemmArgs& a0, hipStream_t st) {
+template <int MODE, bool ZP>
+hipError_t launch_mode_z(const GemmArgs& a0, hipStream_t st) {
   // Few tokens: one wave a workgroup, a thin tile (32 or 64 channels x 16 or
   // 32 tokens), three 128-byte slices in flight, weight loads non-temporal.
   // Three slices rather than four keep 7 (32 x 16) or 3 (64 x 32) workgroups
   // on a CU (LDS-bound), so that the 175B-width decode shapes (N = 49152)
   // run in a single wave of workgroups.
   constexpr int FM = MODE == MODE_FUSED ? MODE_FUSED_X : MODE;
-  if (a0.T <= 16) return launch_cfg<32, 16, 32, 16, 3, 128, FM, true>(a0, st);
-  if (a0.T <= kFewT) return launch_cfg<64, 32, 64, 32, 3, 128, FM, true>(a0, st);
+  if (a0.T <= 16) return launch_cfg<32, 16, 32, 16, 3, 128, FM, true, ZP>(a0, st);
+  if (a0.T <= kFewT) return launch_cfg<64, 32, 64, 32, 3, 128, FM, true, ZP>(a0, st);
   GemmArgs a = a0;
   if (MODE != MODE_FUSED || a.splits < 1 || !a.part) a.splits = 1;
   int64_t cfg = a.cfg, sp = 1;
   if (cfg < 0 || cfg > 1) {  // no plan: the best unsplit configuration
-    choose_wide(a.T, a.N, a.K, false, &cfg, &sp);
+    choose_wide(a.T, a.N, a.K, false, ZP, &cfg, &sp);
     a.splits = 1;
   }
+  // the zero-point epilogue's extra terms do not fit the 320-channel tile's
+  // registers without spilling in the K loop: it runs the 256-channel tiles
+  if (ZP && cfg == 0) return hipErrorInvalidValue;
   if constexpr (MODE == MODE_FUSED) {
     if (a.splits > 1) {  // split K: partial tiles, then one combine launch
       hipError_t e;
-      if (cfg == 0) {
-        e = launch_cfg<320, 256, 80, 128, 2, 128, MODE_PART>(a, st);
-        return e != hipSuccess ? e : launch_cfg<320, 256, 80, 128, 2, 128, MODE_COMBINE>(a, st);
+      if constexpr (!ZP) {
+        if (cfg == 0) {
+          e = launch_cfg<320, 256, 80, 128, 2, 128, MODE_PART>(a, st);
+          return e != hipSuccess ? e : launch_cfg<320, 256, 80, 128, 2, 128, MODE_COMBINE>(a, st);
+        }
       }
       e = launch_cfg<256, 256, 64, 128, 2, 128, MODE_PART>(a, st);
-      return e != hipSuccess ? e : launch_cfg<256, 256, 64, 128, 2, 128, MODE_COMBINE>(a, st);
+      return e != hipSuccess ? e
+                             : launch_cfg<256, 256, 64, 128, 2, 128, MODE_COMBINE, false, ZP>(a, st);
     }
   }
-  if (cfg == 0) return launch_cfg<320, 256, 80, 128, 2, 128, MODE>(a, st);
-  return launch_cfg<256, 256, 64, 128, 2, 128, MODE>(a, st);
+  if constexpr (!ZP) {
+    if (cfg == 0) return launch_cfg<320, 256, 80, 128, 2, 128, MODE>(a, st);
+  }
+  return launch_cfg<256, 256, 64, 128, 2, 128, MODE, false, ZP>(a, st);
+}
+
+template <int MODE>
+hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
+  if constexpr (MODE == MODE_FUSED) {
+    if (a.zp) return launch_mode_z<MODE, true>(a, st);
+  }
+  return launch_mode_z<MODE, false>(a, st);
 }
 }  // namespace
 
 void set_split_override(int64_t splits) { g_split_override.store(splits > 0 ? splits : 0); }
 int64_t split_override() { return g_split_override.load(); }
 
-GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K) {
+GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K, bool zero_point) {
   GemmPlan p{-1, 1, 0, 0};
   if (T <= kFewT || K % 16 != 0 || K <= 0) return p;
-  choose_wide(T, N, K, true, &p.cfg, &p.splits);
+  choose_wide(T, N, K, true, zero_point, &p.cfg, &p.splits);
   p.tiles = ceil_div(N, kCfgBM[p.cfg]) * ceil_div(T, kCfgBN[p.cfg]);
   if (p.splits > 1) p.part_elems = p.splits * p.tiles * kCfgBM[p.cfg] * kCfgBN[p.cfg];
   return p;

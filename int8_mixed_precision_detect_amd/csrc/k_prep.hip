@@ -240,14 +240,17 @@ constexpr int kRowsPerPrepBlock = 1;
 // RPB rows of X per workgroup, 256 / RPB threads (whole waves) per row
 // F16W: the outlier weights are copied from an fp16 weight W16 [N][K]
 // instead of dequantized from CB (the fp16-weight variant of the layer).
-template <bool VEC, int RPB, bool F16W>
+// ZP: zero-point row codes (sx = range / 2 and the offset Z per row, to zp)
+// instead of absmax ones, and the weight-side sum of each channel's outlier
+// codes, osum[j] = sum_o CB[j, O_o] (for the product's offset correction).
+template <bool VEC, int RPB, bool F16W, bool ZP>
 __global__ __launch_bounds__(256) void k_prep(
     const _Float16* __restrict__ X, int64_t T, int64_t K, const uint32_t* __restrict__ mask,
     int32_t* __restrict__ O_out, int32_t* __restrict__ counts, int64_t max_o,
     int8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sx, _Float16* __restrict__ Xo,
     int64_t ldo, int64_t nrowblk, const int8_t* __restrict__ CB, const float* __restrict__ SCB,
     int64_t N, _Float16* __restrict__ Wo, int64_t ocap, int64_t wo_skip,
-    const _Float16* __restrict__ W16) {
+    const _Float16* __restrict__ W16, int32_t* __restrict__ zp, int32_t* __restrict__ osum) {
   // The body uses amdgcn-only types (buffer resources); the host pass only
   // needs the kernel's signature to emit its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(256) void k_prep(
   // Wide outlier sets touch nearly every cache line of a CB row: the channel
   // workgroups then stream whole rows (through the LDS that would hold O)
   // instead of gathering -- see below.
-  const bool wo_stream = !F16W && !row_block && n_use * 64 >= K && K % 16 == 0 && K + 16 <= ocap * 4 &&
+  const bool wo_stream = !F16W && !ZP && !row_block && n_use * 64 >= K && K % 16 == 0 && K + 16 <= ocap * 4 &&
                          K <= 256 * kRowChunks * 16 && (((uintptr_t)CB) & 15) == 0;
   if (listed && !wo_stream) outlier_list<256>(smask, spref, KW, n_use, sO);
   if (blockIdx.x == 0 && counts) {
@@ -340,7 +343,63 @@ __global__ __launch_bounds__(256) void k_prep(
     };
     int8_t* qrow = Xq + (row_ok ? i : 0) * ldq;
     float m = 0.0f;
-    if (VEC) {
+    if (VEC && ZP) {
+      // zero-point: the kept values' range, with 0 in it (outlier columns
+      // zeroed first change neither end), then codes with outliers at 0
+      auto chunk_bits = [&](int64_t c) { return smask[c >> 2] >> (8 * (c & 3)); };
+      float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kCachedChunks; ++u) {
+        const int64_t c = rt + TPR * u;
+        if (c < nc) {
+          cache[u] = zero_masked8(cache[u], chunk_bits(c));
+          minmax8(cache[u], lo, hi);
+        }
+      }
+      if (row_ok)
+        for (int64_t c = rt + TPR * kCachedChunks; c < nc; c += TPR)
+          minmax8(zero_masked8(*(const v8h*)(row + c * 8), chunk_bits(c)), lo, hi);
+      const float hi_r = row_max(hi);
+      __syncthreads();  // row_max's scratch is reused
+      const float lo_r = -row_max(-lo);
+      if (!row_ok) return;
+      const ZpRow z = zp_row(lo_r, hi_r);
+      if (rt == 0) {
+        sx[i] = z.sx;
+        zp[i] = z.Z;
+      }
+#pragma unroll
+      for (int u = 0; u < kCachedChunks; ++u) {
+        const int64_t c = rt + TPR * u;
+        if (c < nc) *(v2u*)(qrow + c * 8) = zp_codes8(cache[u], chunk_bits(c), z);
+      }
+      for (int64_t c = rt + TPR * kCachedChunks; c < nc; c += TPR)
+        *(v2u*)(qrow + c * 8) = zp_codes8(*(const v8h*)(row + c * 8), chunk_bits(c), z);
+      for (int64_t k = K + rt; k < ldq; k += TPR) qrow[k] = 0;
+    } else if (ZP) {
+      float lo = 0.0f, hi = 0.0f;
+      if (row_ok)
+        for (int64_t k = rt; k < K; k += TPR)
+          if (!((smask[k >> 5] >> (k & 31)) & 1u)) {
+            const float x = h2f(row[k]);
+            lo = fminf(lo, x);
+            hi = fmaxf(hi, x);
+          }
+      const float hi_r = row_max(hi);
+      __syncthreads();
+      const float lo_r = -row_max(-lo);
+      if (!row_ok) return;
+      const ZpRow z = zp_row(lo_r, hi_r);
+      if (rt == 0) {
+        sx[i] = z.sx;
+        zp[i] = z.Z;
+      }
+      for (int64_t k = rt; k < ldq; k += TPR) {
+        int8_t q = 0;
+        if (k < K && !((smask[k >> 5] >> (k & 31)) & 1u)) q = (int8_t)zp_code(h2f(row[k]), z);
+        qrow[k] = q;
+      }
+    } else if (VEC) {
       // outlier columns are zeroed in the chunk first (rare); then the row
       // absmax and the codes need no per-element test
       auto chunk_bits = [&](int64_t c) { return smask[c >> 2] >> (8 * (c & 3)); };
@@ -467,6 +526,7 @@ __global__ __launch_bounds__(256) void k_prep(
     const int64_t nr = ceil_div(nch - wave, 4);  // channels wave, wave+4, ...
     const int64_t items = nr * nu;
     int64_t r0 = 0, u0 = 0;  // (channel step, chunk) of the batch's first item
+    int zrun = 0;            // ZP: the current channel's outlier code sum
     for (int64_t q0 = 0; q0 < items; q0 += kGather) {
       int64_t rg[kGather], ug[kGather];
       int64_t rr = r0, uu = u0;
@@ -502,6 +562,20 @@ __global__ __launch_bounds__(256) void k_prep(
           c[g] = (q0 + g < items && o < n_use) ? CB[(j0 + wave + 4 * rg[g]) * K + sO[o]]
                                                : (int8_t)0;
         }
+        if constexpr (ZP) {
+          // a channel's chunks are consecutive items of this wave
+#pragma unroll
+          for (int g = 0; g < kGather; ++g) {
+            const int cs = wave_sum((int)c[g]);
+            if (q0 + g < items) {
+              zrun += cs;
+              if (ug[g] == nu - 1) {
+                if (lane == 0) osum[j0 + wave + 4 * rg[g]] = zrun;
+                zrun = 0;
+              }
+            }
+          }
+        }
 #pragma unroll
         for (int g = 0; g < kGather; ++g) {
           const int64_t o = ug[g] * 64 + lane;
@@ -519,22 +593,58 @@ __global__ __launch_bounds__(256) void k_prep(
       const int8_t* cbrow = CB + j * K;
       const float sj = SCB[j];
       _Float16* worow = Wo + j * ldo;
+      int cs = 0;  // ZP: this lane's part of the channel's outlier code sum
       for (int64_t w = lane; w < KW; w += 64) {
         uint32_t mb = smask[w];
         int64_t o = spref[w];
         while (mb && o < n_use) {
           const int b = __ffs(mb) - 1;
           mb &= mb - 1;
-          if constexpr (F16W)
+          if constexpr (F16W) {
             worow[o++] = W16[j * K + w * 32 + b];
-          else
-            worow[o++] = dequant_weight(cbrow[w * 32 + b], sj);
+          } else {
+            const int c = cbrow[w * 32 + b];
+            if constexpr (ZP) cs += c;
+            worow[o++] = dequant_weight(c, sj);
+          }
         }
+      }
+      if constexpr (ZP) {
+        cs = wave_sum(cs);
+        if (lane == 0) osum[j] = cs;
       }
       for (int64_t o = n_use + lane; o < n_pad; o += 64) worow[o] = (_Float16)0.0f;
     }
   }
 #endif  // __HIP_DEVICE_COMPILE__
+}
+
+// rsum[j] = sum_k CB[j, k]: one wave per row, 16-byte loads when aligned
+__global__ __launch_bounds__(256) void k_rowsum(const int8_t* __restrict__ CB, int64_t N,
+                                                 int64_t K, int32_t* __restrict__ rsum) {
+  const int lane = threadIdx.x & 63;
+  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= N) return;
+  const int8_t* row = CB + j * K;
+  int s = 0;
+  if ((K % 16) == 0 && (((uintptr_t)CB) & 15) == 0) {
+    for (int64_t c = lane; c < K / 16; c += 64) {
+      const v4i v = *(const v4i*)(row + 16 * c);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) s += (int)(int8_t)(v[w] >> (8 * b));
+    }
+  } else {
+    for (int64_t k = lane; k < K; k += 64) s += row[k];
+  }
+  s = wave_sum(s);
+  if (lane == 0) rsum[j] = s;
+}
+
+void launch_rowsum(const int8_t* CB, int64_t N, int64_t K, int32_t* rsum, hipStream_t st) {
+  if (N <= 0) return;
+  k_rowsum<<<dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st>>>(CB, N, K, rsum);
 }
 
 size_t prep_lds_bytes(int64_t K, int64_t ocap) {
@@ -552,17 +662,22 @@ void launch_prep(const PrepArgs& p, hipStream_t st) {
                               (int)lds);
     kern<<<g, dim3(256), lds, st>>>(p.X, p.T, p.K, p.mask, p.O_out, p.counts, p.max_o, p.Xq,
                                     p.ldq, p.sx, p.Xo, p.ldo, nrowblk, p.CB, p.SCB, p.N, p.Wo,
-                                    p.ocap, p.wo_skip, p.W16);
+                                    p.ocap, p.wo_skip, p.W16, p.zp, p.osum);
   };
   if (p.W16) {
     if (p.vec)
-      go(k_prep<true, kRowsPerPrepBlock, true>);
+      go(k_prep<true, kRowsPerPrepBlock, true, false>);
     else
-      go(k_prep<false, kRowsPerPrepBlock, true>);
+      go(k_prep<false, kRowsPerPrepBlock, true, false>);
+  } else if (p.zp) {
+    if (p.vec)
+      go(k_prep<true, kRowsPerPrepBlock, false, true>);
+    else
+      go(k_prep<false, kRowsPerPrepBlock, false, true>);
   } else if (p.vec) {
-    go(k_prep<true, kRowsPerPrepBlock, false>);
+    go(k_prep<true, kRowsPerPrepBlock, false, false>);
   } else {
-    go(k_prep<false, kRowsPerPrepBlock, false>);
+    go(k_prep<false, kRowsPerPrepBlock, false, false>);
   }
 }
 

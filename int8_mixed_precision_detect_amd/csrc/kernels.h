@@ -41,7 +41,13 @@ struct PrepArgs {
   bool vec;         // 16-byte aligned rows of X (K % 8 == 0)
   // fp16 weight [N][K]: Wo copies W16[:, O] instead of dequantizing CB
   const _Float16* W16 = nullptr;
+  // zero-point row codes: the offsets Z [T] out (non-null selects the
+  // scheme) and the per-channel sums of the outlier codes [N] out
+  int32_t* zp = nullptr;
+  int32_t* osum = nullptr;
 };
+// rsum[j] = sum_k CB[j, k] (int32), once per weight (zero-point layer)
+void launch_rowsum(const int8_t* CB, int64_t N, int64_t K, int32_t* rsum, hipStream_t st);
 size_t prep_lds_bytes(int64_t K, int64_t ocap);
 void launch_prep(const PrepArgs& p, hipStream_t st);
 void launch_fill_bias(_Float16* Y, int64_t T, int64_t N, const _Float16* bias, int32_t* counts,
@@ -77,6 +83,11 @@ struct GemmArgs {
   // Wo is already in the workspace (the few-token tiles must not rebuild it
   // from CB: the fp16-weight variant takes it from W)
   bool wo_ready;
+  // zero-point activations (zp non-null): acc + zp[t] * (rsum[j] - osum[j])
+  // is the int8 part (osum read only when there are outlier columns)
+  const int32_t* zp;
+  const int32_t* rsum;
+  const int32_t* osum;
 };
 
 // Any shape and alignment: register-staged, byte-granular loads.
@@ -94,7 +105,8 @@ struct GemmPlan {
   int64_t tiles;       // output tiles
   int64_t part_elems;  // int32 elements of partial accumulators
 };
-GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K);
+// (zero_point: the zero-point layer, which runs the 256-channel tiles only)
+GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K, bool zero_point = false);
 // Process-wide override of the K split (0: the plan's own choice); a test
 // and tuning control.
 void set_split_override(int64_t splits);

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.i8mm_abi_version() == 3
+    assert L.i8mm_abi_version() == 4
     for code, name in [(0, b"I8MM_OK"), (1, b"I8MM_ERR_INVALID_ARG"), (2, b"I8MM_ERR_WORKSPACE"),
                        (3, b"I8MM_ERR_UNSUPPORTED"), (4, b"I8MM_ERR_HIP"),
                        (5, b"I8MM_ERR_OUTLIER_OVERFLOW")]:
@@ -62,7 +62,8 @@ def test_workspace_layout(L):
         regions = [("counts", 16), ("outliers", max(mo, 1) * 4),
                    ("mask", max(math.ceil(K / 32), 1) * 4),
                    ("sx", T * 4), ("xq", T * lay.ldq), ("xo", T * lay.ldo * 2),
-                   ("wo", N * lay.ldo * 2), ("part", 0)]
+                   ("wo", N * lay.ldo * 2), ("zp", max(T, 1) * 4), ("osum", max(N, 1) * 4),
+                   ("part", 0)]
         end = 0
         for name, size in regions:
             off = getattr(lay, name)
@@ -87,14 +88,14 @@ def test_split_k_layout(L):
     assert lay.splits == 2
     tiles = (N // 320) * (T // 256)
     assert lay.total - lay.part >= 2 * tiles * 320 * 256 * 4
-    assert lay.part >= lay.wo + N * lay.ldo * 2
+    assert lay.part >= lay.osum + N * 4 and lay.osum >= lay.zp + T * 4 >= lay.wo + N * lay.ldo * 2
     # the override: clamped to 4, 0 restores the planner's choice
     try:
         for want, got in [(1, 1), (3, 3), (9, 4)]:
             assert L.i8mm_set_split_override(want) == 0
             assert L.int8_linear_workspace_layout(T, N, K, K, ctypes.byref(lay)) == 0
             assert lay.splits == got
-            assert (lay.total > lay.wo + N * lay.ldo * 2 + 4096) == (got > 1)
+            assert (lay.total - lay.part > 0) == (got > 1)
         assert L.i8mm_set_split_override(-1) == 1
     finally:
         assert L.i8mm_set_split_override(0) == 0

@@ -264,6 +264,77 @@ def test_fp16_weight_variant_split_k(i8):
         i8.set_split_override(0)
 
 
+@pytest.mark.parametrize("N,K", [(7, 5), (300, 1024), (65, 1000), (1, 12288)])
+def test_weight_rowsum_exact(i8, N, K):
+    rng = np.random.default_rng(N + K)
+    CB = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    say("weight_rowsum", N, K)
+    got = host(i8.weight_rowsum(dev(CB)))
+    assert np.array_equal(got.astype(np.int64), CB.astype(np.int64).sum(1))
+
+
+def _zp_check(i8, X, W, bias, thr, what):
+    import torch
+    T, K = X.shape
+    N = W.shape[0]
+    say("forward zero-point", what, T, K, N, thr)
+    CBo, SCBo = O.quantize_weight(W)
+    Yo, st = O.linear_forward_zeropoint(X, CBo, SCBo, bias, thr, return_stages=True)
+    CB, SCB = dev(CBo), dev(SCBo)
+    rsum = i8.weight_rowsum(CB)
+    ws = i8.alloc_workspace(T, N, K)
+    Y = i8.linear_forward_zeropoint(dev(X), CB, SCB, rsum, None if bias is None else dev(bias),
+                                    thr, workspace=ws)
+    torch.cuda.synchronize()
+    err = assert_y_close(host(Y), Yo, what)
+    v = _ws_views(i8, ws, T, N, K, K)
+    n = len(st["O"])
+    assert v["counts"][0] == n
+    assert np.array_equal(v["O"], st["O"].astype(np.int32))
+    assert np.array_equal(v["sx"].view(np.uint32), st["sx"].view(np.uint32))
+    assert np.array_equal(v["Xq"][:, :K], st["Xq"])
+    lay = i8.workspace_layout(T, N, K)
+    b = host(ws)
+    zp = b[lay["zp"]: lay["zp"] + 4 * T].view(np.int32)
+    assert np.array_equal(zp, st["Z"])
+    assert np.array_equal(v["Xo"][:, :n].view(np.uint16), st["Xo"].view(np.uint16))
+    assert np.array_equal(v["Wo"][:, :n].view(np.uint16), st["Wo"].view(np.uint16))
+    if n:
+        osum = b[lay["osum"]: lay["osum"] + 4 * N].view(np.int32)
+        assert np.array_equal(osum.astype(np.int64), CBo[:, st["O"]].astype(np.int64).sum(1))
+    return err
+
+
+@pytest.mark.parametrize("T,K,N,planted,thr,relu", [
+    (300, 1024, 517, 3, 6.0, False),   # wide tiles
+    (300, 1024, 517, 3, 6.0, True),    # one-signed rows: Z = 127
+    (5, 1040, 70, 40, 6.0, True),      # few tokens (Wo from step 2, fp16 tail)
+    (17, 12288, 300, 12, 6.0, False),
+    (32, 2048, 1000, 6, 6.0, True),
+    (16, 2048, 300, 0, 2.5, False),    # few tokens, > 128 outlier columns
+    (40, 1000, 130, 5, 6.0, True),     # K not a multiple of 16: the generic product
+    (64, 256, 96, 0, 1e-6, False),     # every column an outlier
+    (2048, 512, 640, 4, 6.0, True),    # several waves of wide tiles
+])
+def test_zero_point_variant(i8, T, K, N, planted, thr, relu):
+    d = make_random_case(T * 3 + K + N + 29, T, K, N, n_planted=planted, bias=True)
+    X = d["X"].copy()
+    if relu:
+        X = np.abs(X)
+        X[1] = 0                     # an all-zero row: S = Z = sx = 0
+    _zp_check(i8, X, d["W"], d["bias"], thr, f"zero-point {T}x{K}x{N} thr={thr} relu={relu}")
+
+
+def test_zero_point_variant_split_k(i8):
+    d = make_random_case(78, 300, 4112, 700, n_planted=5, bias=True)
+    try:
+        i8.set_split_override(2)
+        assert i8.workspace_layout(300, 700, 4112)["splits"] == 2
+        _zp_check(i8, np.abs(d["X"]), d["W"], d["bias"], 6.0, "zero-point, split K x2")
+    finally:
+        i8.set_split_override(0)
+
+
 def test_outlier_overflow_is_reported(i8):
     d = make_random_case(904, 64, 256, 64, n_planted=10)
     say("forward overflow")
