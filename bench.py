@@ -42,6 +42,9 @@ def kernel_fingerprint() -> str:
     return h.hexdigest()[:16]
 
 
+ENTRY = {"int8": "int8_linear_forward", "fp16w": "int8_linear_forward_fp16w",
+         "zeropoint": "int8_linear_forward_zeropoint"}
+
 WORKLOAD_DESC = {
     "tiny": "tiny (16 tokens, 64 x 64 LLM.int8() linear)",
     "6.7b": "6.7b-scale first FF layer (LLM.int8() linear)",
@@ -55,10 +58,15 @@ WORKLOAD_DESC = {
 }
 
 
-def read_traffic(workload: str):
+def profile_tag(workload: str, layer: str) -> str:
+    return workload if layer == "int8" else f"{workload}-{layer}"
+
+
+def read_traffic(workload: str, layer: str = "int8"):
     """HBM bytes per launch of the product kernel from the committed counter
     summary, or None when it is missing or was taken on other kernel source."""
-    path = TRAFFIC_FILE.format(workload)
+    tag = profile_tag(workload, layer)
+    path = TRAFFIC_FILE.format(tag)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -67,7 +75,7 @@ def read_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, _, v = line.partition(":")
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_fingerprint") != kernel_fingerprint() or kv.get("workload") != workload:
+    if kv.get("kernel_fingerprint") != kernel_fingerprint() or kv.get("workload") != tag:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -75,7 +83,7 @@ def read_traffic(workload: str):
         return None
 
 
-def cpu_baseline(d, cols: int, reps: int):
+def cpu_baseline(d, cols: int, reps: int, layer: str = "int8"):
     """The oracle as it stands, on all rows and the first `cols` output channels."""
     import numpy as np
     import oracle.llm_int8 as O
@@ -86,7 +94,12 @@ def cpu_baseline(d, cols: int, reps: int):
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        O.linear_forward(X, CB, SCB, b, thr)
+        if layer == "fp16w":
+            O.linear_forward_fp16w(X, W[:cols], b, thr)
+        elif layer == "zeropoint":
+            O.linear_forward_zeropoint(X, CB, SCB, b, thr)
+        else:
+            O.linear_forward(X, CB, SCB, b, thr)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     threads = None
@@ -109,6 +122,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="13b")
+    ap.add_argument("--layer", choices=("int8", "fp16w", "zeropoint"), default="int8",
+                    help="int8 weight (default); fp16 weight kept and quantized per call; "
+                         "zero-point activation codes")
     ap.add_argument("--copies", type=int, default=3,
                     help="rotate this many copies of X/CB/SCB/Y so the 256 MB last-level "
                          "cache cannot hold one step's inputs from the step before")
@@ -137,7 +153,7 @@ def main() -> int:
     torch.cuda.set_device(dev)
 
     copies = max(1, args.copies)
-    Xs, CBs, SCBs, Ys = [], [], [], []
+    Xs, CBs, SCBs, Ys, Ws, RSs = [], [], [], [], [], []
     Wd = torch.from_numpy(d["W"]).to(dev)
     for _ in range(copies):
         Xs.append(torch.from_numpy(d["X"]).to(dev))
@@ -145,13 +161,24 @@ def main() -> int:
         CBs.append(CB)
         SCBs.append(SCB)
         Ys.append(torch.empty((T, N), dtype=torch.float16, device=dev))
+        if args.layer == "fp16w":
+            Ws.append(Wd.clone())
+        if args.layer == "zeropoint":
+            RSs.append(i8.weight_rowsum(CB))
     bias = None if d["bias"] is None else torch.from_numpy(d["bias"]).to(dev)
     ws = i8.alloc_workspace(T, N, K, None, dev)
     torch.cuda.synchronize()
 
     def step(s):
         c = s % copies
-        i8.linear_forward(Xs[c], CBs[c], SCBs[c], bias, wl.threshold, workspace=ws, out=Ys[c])
+        if args.layer == "fp16w":
+            i8.linear_forward_fp16w(Xs[c], Ws[c], bias, wl.threshold, workspace=ws, out=Ys[c],
+                                    CB=CBs[c], SCB=SCBs[c])
+        elif args.layer == "zeropoint":
+            i8.linear_forward_zeropoint(Xs[c], CBs[c], SCBs[c], RSs[c], bias, wl.threshold,
+                                        workspace=ws, out=Ys[c])
+        else:
+            i8.linear_forward(Xs[c], CBs[c], SCBs[c], bias, wl.threshold, workspace=ws, out=Ys[c])
 
     for s in range(args.warmup):
         step(s)
@@ -189,7 +216,7 @@ def main() -> int:
     ops = 2.0 * T * N * K
     tops = ops / (ms_per_step * 1e-3) / 1e12
     gemm_ms = stage_avg[2]
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(args.workload, args.layer)
     n_pad = -(-n_o // 32) * 32
     ldq = -(-K // 64) * 64
     if T <= 32:
@@ -221,7 +248,7 @@ def main() -> int:
         quant_bytes += N * n_o + 2 * N * n_pad
 
     result = {
-        "metric": "effective TOPS (2TNK/s) of int8_linear_forward at T=2048; % int8 MFMA peak",
+        "metric": f"effective TOPS (2TNK/s) of {ENTRY[args.layer]} at T=2048; % int8 MFMA peak",
         "value": round(tops, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -236,7 +263,7 @@ def main() -> int:
         "config": {"workload": WORKLOAD_DESC.get(args.workload, args.workload),
                    "T": T, "K": K, "N": N, "threshold": wl.threshold, "n_outliers": n_o,
                    "bias": d["bias"] is not None, "buffer_copies": copies,
-                   "k_splits": i8.workspace_layout(T, N, K)["splits"]},
+                   "k_splits": i8.workspace_layout(T, N, K)["splits"], "layer": args.layer},
         "roofline": roofline,
         "stages_ms": {"detect": round(stage_avg[0], 5), "quantize_gather": round(stage_avg[1], 5),
                       "product": round(stage_avg[2], 5), "whole_call": round(stage_avg[3], 5)},
@@ -276,7 +303,8 @@ def main() -> int:
         result["copy_calibration_bytes"] = nbytes
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d, min(args.cpu_cols, N), max(1, args.cpu_reps))
+        result["cpu_baseline"] = cpu_baseline(d, min(args.cpu_cols, N), max(1, args.cpu_reps),
+                                              args.layer)
 
     print(json.dumps(result), flush=True)
     return 0

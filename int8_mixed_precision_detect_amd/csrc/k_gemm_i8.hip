@@ -633,15 +633,41 @@ constexpr int64_t kCfgBM[2] = {320, 256}, kCfgBN[2] = {256, 256};
 constexpr int64_t kMaxSplits = 4;
 constexpr int64_t kMinSplitK = 1024;  // bytes of K a split walks at least
 
-// The workgroups run in waves of one per CU, and a workgroup's time is about
-// its tile area times the 128-byte slices of K it walks, so a launch costs
-// about ceil(tiles * splits / CUs) * area * ceil(slices / splits), with 5 %
-// added for the exchange of partial sums (a second launch) when K is split.  The host takes
-// the cheapest (ties: fewer splits, then configuration 1).  The 13B-scale
-// layer (20480 x 2048 outputs, K = 5120) runs 512 tiles of configuration 0
-// in two full waves (configuration 1 would need 640 tiles, 2.5 waves); the
-// 13B down projection (5120 x 2048 outputs, K = 20480) has only 128 tiles,
-// so K is split in two: 256 workgroups, one full wave.
+// Planner: a modelled duration (microseconds) for each configuration and
+// split count, the smallest taken (ties: fewer splits, then configuration 1).
+// The workgroups run in rounds of one per CU; one walks ceil(slices / splits)
+// 128-byte slices of K at kSliceUs each, plus kItemUs of set-up and epilogue;
+// a round that fills every CU runs kFullRound times slower (the workgroups
+// share the last-level cache and fabric).  Splitting K adds the partial
+// tiles: written once per round of the split launch (kPartWriteUs a KB), read
+// back by the combine launch, whose ceil(tiles / CUs) rounds each read
+// `splits` partial tiles per CU (kPartReadUs a KB).  The constants are
+// fitted to the measured durations of both tiles on MI355X over T = 64-2048,
+// K = 4096-20480, N = 5120-20480 and 1-4 splits; the model picks the
+// fastest measured choice on all of them but one (within 0.3 %).  So the 13B
+// first feed-forward layer (20480 x 2048 outputs, K = 5120) runs 512 tiles
+// of configuration 0 in two rounds, its attention projection (5120 x 2048,
+// K = 5120) 160 tiles of configuration 1 unsplit, and the down projection
+// (5120 x 2048, K = 20480) splits K in two over 128 tiles of configuration 0.
+constexpr double kSliceUs[2] = {1.54, 1.36}, kItemUs[2] = {25.0, 20.0};
+constexpr double kFullRound[2] = {1.22, 1.085};
+constexpr double kPartWriteUs = 0.0095, kPartReadUs = 0.032;
+
+double plan_cost(int64_t T, int64_t N, int64_t K, int c, int64_t sp, int64_t cus) {
+  const int64_t tiles = ceil_div(N, kCfgBM[c]) * ceil_div(T, kCfgBN[c]);
+  const int64_t items = tiles * sp;
+  const int64_t slices = ceil_div(K, 128) > 0 ? ceil_div(K, 128) : 1;
+  const double rounds = (double)ceil_div(items, cus);
+  double t = rounds * ((double)ceil_div(slices, sp) * kSliceUs[c] + kItemUs[c]) *
+             (items >= cus ? kFullRound[c] : 1.0);
+  if (sp > 1) {
+    const double tile_kb = (double)(kCfgBM[c] * kCfgBN[c] * 4) / 1024.0;
+    t += rounds * tile_kb * kPartWriteUs +
+         (double)ceil_div(tiles, cus) * (double)sp * tile_kb * kPartReadUs;
+  }
+  return t;
+}
+
 void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split, bool only_cfg1,
                  int64_t* cfg, int64_t* splits) {
   const int64_t cus = cu_count();
@@ -658,9 +684,7 @@ void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split, bool only_cf
     if (ovr > 0 && sp != want) continue;
     if (ovr == 0 && sp > 1 && (ceil_div(K, sp) < kMinSplitK || sp > slices)) continue;
     for (int c = 1; c >= (only_cfg1 ? 1 : 0); --c) {
-      const int64_t tiles = ceil_div(N, kCfgBM[c]) * ceil_div(T, kCfgBN[c]);
-      const double cost = (double)ceil_div(tiles * sp, cus) * (double)(kCfgBM[c] * kCfgBN[c]) *
-                          (double)ceil_div(slices, sp) * (sp > 1 ? 1.05 : 1.0);
+      const double cost = plan_cost(T, N, K, c, sp, cus);
       if (first || cost < best) {
         best = cost;
         *cfg = c;

@@ -103,6 +103,23 @@ def test_split_k_layout(L):
     assert lay.splits == 2
 
 
+@pytest.mark.parametrize("T,N,K,splits", [
+    (2048, 20480, 5120, 1),   # 13B first FF layer: 512 tiles, two full rounds
+    (2048, 5120, 5120, 1),    # attention projection: 160 tiles, one round
+    (2048, 16384, 4096, 1),   # 6.7B first FF layer
+    (1024, 5120, 5120, 2),
+    (256, 5120, 20480, 4),    # K-heavy, few tokens: 20 tiles
+    (128, 5120, 5120, 2),
+])
+def test_planner_choices(L, T, N, K, splits):
+    # the split counts the planner's duration model picks for 256 compute
+    # units (the fastest measured on MI355X for these shapes)
+    from int8_mixed_precision_detect_amd._lib import WsLayout
+    lay = WsLayout()
+    assert L.int8_linear_workspace_layout(T, N, K, K, ctypes.byref(lay)) == 0
+    assert lay.splits == splits
+
+
 def test_invalid_arguments_are_rejected_on_the_host(L):
     nan = float("nan")
     fwd = L.int8_linear_forward
