@@ -44,11 +44,9 @@ i8mm_status layout_of(int64_t T, int64_t N, int64_t K, int64_t max_o, i8mm_ws_la
   L->wo = take((size_t)N * (size_t)L->ldo * 2);
   L->zp = take((size_t)(T > 0 ? T : 1) * 4);
   L->osum = take((size_t)(N > 0 ? N : 1) * 4);
-  // partial tiles: room for the plans of both layers (the zero-point one
-  // runs only the 256-channel tiles)
+  // partial tiles of the product's plan (both layer variants share it)
   const GemmPlan gp = plan_gemm_i8(T, N, K);
-  const GemmPlan gz = plan_gemm_i8(T, N, K, true);
-  L->part = take((size_t)(gp.part_elems > gz.part_elems ? gp.part_elems : gz.part_elems) * 4);
+  L->part = take((size_t)gp.part_elems * 4);
   L->splits = gp.splits;
   L->total = off;
   return I8MM_OK;
@@ -208,7 +206,7 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   a.max_o = max_outliers;
   a.bias = (const _Float16*)bias;
   a.Y = (_Float16*)Y;
-  const GemmPlan gp = plan_gemm_i8(T, N, K, rsum != nullptr);
+  const GemmPlan gp = plan_gemm_i8(T, N, K);
   a.cfg = gp.cfg;
   a.splits = gp.splits;
   a.part = gp.part_elems > 0 ? (int32_t*)(w + L.part) : nullptr;

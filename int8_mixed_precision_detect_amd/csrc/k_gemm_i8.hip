@@ -156,8 +156,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       const bool isA = j < ACH;
       const int rr = (isA ? j : j - ACH) * RPP + ln / CPR;
       static_assert(RPP % 8 == 0, "swizzle period");
-      const int64_t g = isA ? min(m0 + rr, a.N - 1) : min(n0 + rr, a.T - 1);
-      voff[u] = (uint32_t)(g * (isA ? ldab : ldbb) + kc);
+      // 32-bit arithmetic: the offset is the low 32 bits either way (a
+      // buffer resource spans less than 4 GB), and 32-bit values keep
+      // fewer registers live across the K loop
+      const uint32_t g = (uint32_t)(isA ? min(m0 + rr, a.N - 1) : min(n0 + rr, a.T - 1));
+      voff[u] = g * (uint32_t)(isA ? ldab : ldbb) + (uint32_t)kc;
     }
   };
   auto lds_dst = [&](int buf, int u) {
@@ -439,17 +442,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     return;
   }
 
-  const int lrow = 4 * (lane >> 4);  // first of the 4 channels a lane holds
-  const int lcol = lane & 15;        // token within a 16-wide block
+  // (opaque copies of the lane's position: the epilogue's indices are
+  // computed here and again after the outlier loop, not hoisted above the
+  // loops and kept -- spilled -- across them)
+  int lrow = 4 * (lane >> 4);  // first of the 4 channels a lane holds
+  int lcol = lane & 15;        // token within a 16-wide block
+  asm volatile("" : "+v"(lrow), "+v"(lcol));
+  const int m0i = (int)m0, n0i = (int)n0;  // T, N < 2^31
 
   if constexpr (MODE == MODE_I32) {
     const bool cvec = ((a.N & 3) == 0) && ((((uintptr_t)a.C) & 15) == 0);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int64_t f = m0 + wm0 + i * 16 + lrow;
+      const int f = m0i + wm0 + i * 16 + lrow;
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const int64_t t = n0 + wn0 + j * 16 + lcol;
+        const int t = n0i + wn0 + j * 16 + lcol;
         if (t >= a.T) continue;
         int32_t* dst = a.C + t * a.N + f;
         if (cvec && f + 3 < a.N) {
@@ -467,7 +475,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     float sxv[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int64_t t = n0 + wn0 + j * 16 + lcol;
+      const int t = n0i + wn0 + j * 16 + lcol;
       // clamped, unconditional loads: all in flight together
       const float v = a.sx[t < a.T ? t : a.T - 1];
       sxv[j] = (t < a.T) ? v : 0.0f;
@@ -476,7 +484,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t f = m0 + wm0 + i * 16 + lrow + r;
+        const int f = m0i + wm0 + i * 16 + lrow + r;
         const float sv = a.SCB[f < a.N ? f : a.N - 1];
         const float sc = f < a.N ? sv * (1.0f / 16129.0f) : 0.0f;
         // int32 accumulator -> fp32 acc * sx * SCB / 127^2, in place
@@ -523,6 +531,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       // (prefetched: its one slice is in flight in buffer tail_buf)
       run(F16Slices{}, 0, Kt, [] {}, tail_buf, tail_pre ? 1 : 0);
     }
+    asm volatile("" : "+v"(lrow), "+v"(lcol));
     const bool yvec = ((a.N & 3) == 0) && ((((uintptr_t)a.Y) & 7) == 0);
     // Zero-point activations: the offset part of the int8 product,
     // (sx Z / 127) (SCB R / 127) with R the channel's kept-column code sum,
@@ -533,7 +542,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     if constexpr (ZP) {
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const int64_t t = n0 + wn0 + j * 16 + lcol;
+        const int t = n0i + wn0 + j * 16 + lcol;
         const int64_t tc = t < a.T ? t : a.T - 1;
         const float sxt = a.sx[tc];
         const int z = a.zp[tc];
@@ -542,7 +551,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int64_t f = m0 + wm0 + i * 16 + lrow;  // 4 consecutive channels
+      const int f = m0i + wm0 + i * 16 + lrow;  // 4 consecutive channels
       float vr[ZP ? 4 : 1];
       if constexpr (ZP) {
 #pragma unroll
@@ -574,17 +583,72 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       }
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
-        const int64_t t = n0 + wn0 + j * 16 + lcol;
-        if (t >= a.T) continue;
         const v4f v = __builtin_bit_cast(v4f, acc[i][j]);
-        v4h y;
+        v4f w;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (ZP)
-            y[r] = (_Float16)(v[r] + bv[r] + ut[j] * vr[r]);
+            w[r] = v[r] + bv[r] + ut[j] * vr[r];
           else
-            y[r] = (_Float16)(v[r] + bv[r]);
+            w[r] = v[r] + bv[r];
         }
+        acc[i][j] = __builtin_bit_cast(v4i, w);
+      }
+    }
+    // Wide tiles with N a multiple of 8: Y goes out through LDS, 64 tokens
+    // of the tile at a time, as whole 16-byte chunks of token rows, so that
+    // every line of Y is written completely by one workgroup at once.
+    bool staged = false;
+    if constexpr (MODE != MODE_FUSED_X) {
+      staged = ((a.N & 7) == 0) && ((((uintptr_t)a.Y) & 15) == 0);
+      if (staged) {
+        constexpr int JP = 2, RW = NWN * JP * 16, LDH = BM + 8, CH = BM / 8, TOT = RW * CH;
+        static_assert(NI % JP == 0 && TOT % (NWAVE * 64) == 0, "staging passes");
+        static_assert(RW * LDH * 2 <= S * STAGE, "staging fits the slice buffers");
+        _Float16* sy = (_Float16*)lds;
+        __syncthreads();  // every wave is done with the slices in LDS
+#pragma unroll
+        for (int q = 0; q < NI / JP; ++q) {
+#pragma unroll
+          for (int jj = 0; jj < JP; ++jj) {
+            const int row = (wave % NWN) * (JP * 16) + jj * 16 + lcol;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+              const v4f v = __builtin_bit_cast(v4f, acc[i][q * JP + jj]);
+              v4h y;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) y[r] = (_Float16)v[r];
+              *(v4h*)(sy + row * LDH + wm0 + i * 16 + lrow) = y;
+            }
+          }
+          __syncthreads();
+#pragma unroll
+          for (int c0 = 0; c0 < TOT; c0 += NWAVE * 64) {
+            const int c = c0 + tid, row = c / CH, ch = c % CH;
+            const int64_t t = n0 + (row / (JP * 16)) * WN + q * (JP * 16) + row % (JP * 16);
+            const int64_t f = m0 + ch * 8;
+            const v4i val = *(const v4i*)(sy + row * LDH + ch * 8);
+            if (t < a.T && f < a.N) *(v4i*)(a.Y + t * a.N + f) = val;
+          }
+          __syncthreads();
+        }
+      }
+    }
+    // otherwise: a token's channels of the wave tile (the MI 32-byte pieces
+    // of its row segment) go out back to back, so that each line of Y is
+    // complete in the cache before it is written back
+    if (!staged)
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int t = n0i + wn0 + j * 16 + lcol;
+      if (t >= a.T) continue;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int f = m0i + wm0 + i * 16 + lrow;
+        const v4f v = __builtin_bit_cast(v4f, acc[i][j]);
+        v4h y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = (_Float16)v[r];
         _Float16* dst = a.Y + t * a.N + f;
         if (yvec && f + 3 < a.N) {
           *(v4h*)dst = y;
@@ -668,7 +732,7 @@ double plan_cost(int64_t T, int64_t N, int64_t K, int c, int64_t sp, int64_t cus
   return t;
 }
 
-void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split, bool only_cfg1,
+void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split,
                  int64_t* cfg, int64_t* splits) {
   const int64_t cus = cu_count();
   const int64_t slices = ceil_div(K, 128) > 0 ? ceil_div(K, 128) : 1;
@@ -683,7 +747,7 @@ void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split, bool only_cf
   for (int64_t sp = 1; sp <= kMaxSplits; ++sp) {
     if (ovr > 0 && sp != want) continue;
     if (ovr == 0 && sp > 1 && (ceil_div(K, sp) < kMinSplitK || sp > slices)) continue;
-    for (int c = 1; c >= (only_cfg1 ? 1 : 0); --c) {
+    for (int c = 1; c >= 0; --c) {
       const double cost = plan_cost(T, N, K, c, sp, cus);
       if (first || cost < best) {
         best = cost;
@@ -709,29 +773,22 @@ hipError_t launch_mode_z(const GemmArgs& a0, hipStream_t st) {
   if (MODE != MODE_FUSED || a.splits < 1 || !a.part) a.splits = 1;
   int64_t cfg = a.cfg, sp = 1;
   if (cfg < 0 || cfg > 1) {  // no plan: the best unsplit configuration
-    choose_wide(a.T, a.N, a.K, false, ZP, &cfg, &sp);
+    choose_wide(a.T, a.N, a.K, false, &cfg, &sp);
     a.splits = 1;
   }
-  // the zero-point epilogue's extra terms do not fit the 320-channel tile's
-  // registers without spilling in the K loop: it runs the 256-channel tiles
-  if (ZP && cfg == 0) return hipErrorInvalidValue;
   if constexpr (MODE == MODE_FUSED) {
     if (a.splits > 1) {  // split K: partial tiles, then one combine launch
       hipError_t e;
-      if constexpr (!ZP) {
-        if (cfg == 0) {
-          e = launch_cfg<320, 256, 80, 128, 2, 128, MODE_PART>(a, st);
-          return e != hipSuccess ? e : launch_cfg<320, 256, 80, 128, 2, 128, MODE_COMBINE>(a, st);
-        }
+      if (cfg == 0) {
+        e = launch_cfg<320, 256, 80, 128, 2, 128, MODE_PART>(a, st);
+        return e != hipSuccess ? e : launch_cfg<320, 256, 80, 128, 2, 128, MODE_COMBINE, false, ZP>(a, st);
       }
       e = launch_cfg<256, 256, 64, 128, 2, 128, MODE_PART>(a, st);
       return e != hipSuccess ? e
                              : launch_cfg<256, 256, 64, 128, 2, 128, MODE_COMBINE, false, ZP>(a, st);
     }
   }
-  if constexpr (!ZP) {
-    if (cfg == 0) return launch_cfg<320, 256, 80, 128, 2, 128, MODE>(a, st);
-  }
+  if (cfg == 0) return launch_cfg<320, 256, 80, 128, 2, 128, MODE, false, ZP>(a, st);
   return launch_cfg<256, 256, 64, 128, 2, 128, MODE, false, ZP>(a, st);
 }
 
@@ -747,10 +804,10 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
 void set_split_override(int64_t splits) { g_split_override.store(splits > 0 ? splits : 0); }
 int64_t split_override() { return g_split_override.load(); }
 
-GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K, bool zero_point) {
+GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K) {
   GemmPlan p{-1, 1, 0, 0};
   if (T <= kFewT || K % 16 != 0 || K <= 0) return p;
-  choose_wide(T, N, K, true, zero_point, &p.cfg, &p.splits);
+  choose_wide(T, N, K, true, &p.cfg, &p.splits);
   p.tiles = ceil_div(N, kCfgBM[p.cfg]) * ceil_div(T, kCfgBN[p.cfg]);
   if (p.splits > 1) p.part_elems = p.splits * p.tiles * kCfgBM[p.cfg] * kCfgBN[p.cfg];
   return p;

@@ -105,8 +105,7 @@ struct GemmPlan {
   int64_t tiles;       // output tiles
   int64_t part_elems;  // int32 elements of partial accumulators
 };
-// (zero_point: the zero-point layer, which runs the 256-channel tiles only)
-GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K, bool zero_point = false);
+GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K);
 // Process-wide override of the K split (0: the plan's own choice); a test
 // and tuning control.
 void set_split_override(int64_t splits);
