@@ -51,6 +51,9 @@ namespace {
 // a range of K and store their int32 accumulators in a.part; one combine
 // workgroup a tile loads and adds them (exact) and runs the fused epilogue.
 constexpr int MODE_I32 = 0, MODE_FUSED = 1, MODE_FUSED_X = 2, MODE_PART = 3, MODE_COMBINE = 4;
+struct NoDma {
+  __device__ void operator()(int) const {}
+};
 // LDS beyond the slices for MODE_FUSED_X: the outlier list and the tile's
 // X[:, O] values ([kFewOcap][BN] halves)
 constexpr size_t few_lds(int BN) { return (size_t)kFewOcap * 4 + (size_t)kFewOcap * BN * 2; }
@@ -106,6 +109,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   constexpr int ACH = BM / RPP, BCH = BN / RPP;  // load instructions per slice
   constexpr int PW = (ACH + BCH) / NWAVE;        // ... per wave
   constexpr int KS = KB / 64;                    // MFMA k-steps per slice
+  // wide tiles issue each slice refill among the MFMAs of the slice before
+  constexpr bool kInterleave = MODE != MODE_FUSED_X && (WM / 16) * (WN / 16) > 32;
   static_assert(KB == 64 || KB == 128, "slice width");
   static_assert(S >= 2 && S <= 6 && (S - 1) * PW < 64, "slices in flight");
   static_assert(MODE != MODE_FUSED_X || (NWAVE == 1 && BM <= 64), "one wave, one lane a row");
@@ -212,8 +217,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x, y, acc[i][j], 0, 0, 0);
     }
   };
-  // the MFMAs of one slice; the other waves of the SIMD cover LDS latency
-  auto compute = [&](auto f16, int buf) {
+  // the MFMAs of one slice; the other waves of the SIMD cover LDS latency.
+  // dma(u), when given, issues piece u of a slice refill: the wide tiles
+  // interleave the PW pieces with the first MFMAs of the slice, one piece per
+  // NI/2 MFMAs, so that a wave keeps its MFMA pipe busy while the CU's
+  // address unit works through the workgroup's refill queue (issued in one
+  // burst, the pieces held every wave's MFMAs back until its own were
+  // accepted).
+  auto compute = [&](auto f16, int buf, auto&& dma_piece) {
+    constexpr bool kDma = !std::is_same_v<std::decay_t<decltype(dma_piece)>, NoDma>;
+
     const char* As = lds + buf * STAGE;
     const char* Bs = As + BM * KB;
 #pragma unroll
@@ -244,9 +257,24 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
             fa1 = *(const v4i*)(As + frag_off(wm0 + (i + 1) * 16, h));
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
+          if constexpr (kDma) {
+            static_assert(NI % 2 == 0 && 2 * MI * KS >= PW, "refill slots");
 #pragma unroll
-          for (int j = 0; j < NI; ++j) mma(f16, i, j, fa0, fb[j]);
-          __builtin_amdgcn_sched_group_barrier(0x008, NI, 0);
+            for (int jh = 0; jh < 2; ++jh) {
+#pragma unroll
+              for (int j = jh * (NI / 2); j < (jh + 1) * (NI / 2); ++j) mma(f16, i, j, fa0, fb[j]);
+              __builtin_amdgcn_sched_group_barrier(0x008, NI / 2, 0);
+              const int slot = (h * MI + i) * 2 + jh;
+              if (slot < PW) {
+                dma_piece(slot);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) mma(f16, i, j, fa0, fb[j]);
+            __builtin_amdgcn_sched_group_barrier(0x008, NI, 0);
+          }
           fa0 = fa1;
         }
       }
@@ -393,7 +421,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       // one barrier: slice kt is visible to every wave, and every wave is
       // done with slice kt-1, whose buffer is refilled with slice kt-1+S
       __builtin_amdgcn_s_barrier();
-      if (kt >= 1 && kt - 1 + S < nk) issue((int)((b0 + kt - 1) % S), kb + (kt - 1 + S) * KB, Kb);
+      const bool refill = kt >= 1 && kt - 1 + S < nk;
+      if constexpr (!kInterleave) {
+        if (refill) issue((int)((b0 + kt - 1) % S), kb + (kt - 1 + S) * KB, Kb);
+      }
       if constexpr (MODE == MODE_FUSED && !decltype(f16)::value) {
         // the last slice: buffer (kt + 1) % S held slice kt + 1 - S, done.
         // (An opaque copy of the flag, so that the compiler does not version
@@ -404,7 +435,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       }
       if constexpr (MODE == MODE_FUSED_X && !decltype(f16)::value)
         extract((int)((b0 + kt) % S), kb + kt * KB);
-      compute(f16, (int)((b0 + kt) % S));
+      if constexpr (kInterleave) {
+        // The refill of slice kt-1+S goes out among the MFMAs of slice kt (a
+        // ragged last slice reads zeros past Kb).  Iterations without one
+        // issue the same pieces as no-ops -- out-of-range offsets, which
+        // read nothing, into a spare 1 KB of LDS -- so that the loop body
+        // is one block.
+        const int64_t k0 = kb + (kt - 1 + S) * KB;
+        const int rem = !refill ? 0 : k0 + KB <= Kb ? KB : (int)(Kb - k0);
+        const int rb = (int)((b0 + kt - 1 + S) % S);
+        compute(f16, (int)((b0 + kt) % S), [&](int u) {
+          void* dst = refill ? (void*)lds_dst(rb, u) : (void*)(lds + S * STAGE);
+          dma(u, dst, kc < rem ? voff[u] : 0x80000000u, refill ? k0 : 0);
+        });
+      } else {
+        compute(f16, (int)((b0 + kt) % S), NoDma{});
+      }
       // keeps the epilogue's loads (scales, bias) below the loop instead of
       // hoisted above it, where they would hold registers throughout
       asm volatile("" ::: "memory");
@@ -668,7 +714,9 @@ template <int BM, int BN, int WM, int WN, int S, int KB, int MODE, bool NTA = fa
           bool ZP = false>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  constexpr size_t LDS = (size_t)S * (BM + BN) * KB + (MODE == MODE_FUSED_X ? few_lds(BN) : 0);
+  constexpr bool kWide = MODE != MODE_FUSED_X && (WM / 16) * (WN / 16) > 32;
+  constexpr size_t LDS = (size_t)S * (BM + BN) * KB + (MODE == MODE_FUSED_X ? few_lds(BN) : 0) +
+                         (kWide ? 1024 : 0);  // the no-op refills' target
   auto kern = k_gemm_i8<BM, BN, WM, WN, S, KB, MODE, NTA, ZP>;
   hipError_t e = hipFuncSetAttribute((const void*)kern,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
