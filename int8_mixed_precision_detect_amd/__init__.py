@@ -25,7 +25,7 @@ __all__ = [
     "linear_forward_zeropoint", "workspace_layout",
     "workspace_size",
     "alloc_workspace", "linear_status", "find_outliers", "quantize_rows", "outlier_weights",
-    "gemm_s32", "profile_enable", "profile_read", "set_split_override", "Int8Linear",
+    "gemm_s32", "profile_enable", "profile_read", "set_split_override", "set_tile_override", "Int8Linear",
 ]
 
 DEFAULT_THRESHOLD = 6.0
@@ -265,6 +265,13 @@ def gemm_s32(A: torch.Tensor, B: torch.Tensor, K: Optional[int] = None) -> torch
           lib().int8_gemm_s32(_ptr(A), A.shape[1], _ptr(B), B.shape[1], _ptr(C), T, N, K,
                               _stream(A)))
     return C
+
+
+def set_tile_override(cfg: int = -1) -> None:
+    """Output tile of the product at T > 32 (0: 320 x 256, 1: 256 x 256,
+    2: 192 x 256); -1 = the library's choice.  Process-wide; size workspaces
+    under the same setting."""
+    check("i8mm_set_tile_override", lib().i8mm_set_tile_override(int(cfg)))
 
 
 def set_split_override(splits: int = 0) -> None:

@@ -87,6 +87,12 @@ i8mm_status i8mm_set_split_override(int64_t splits) {
   return I8MM_OK;
 }
 
+i8mm_status i8mm_set_tile_override(int64_t cfg) {
+  if (cfg < -1 || cfg > 2) return I8MM_ERR_INVALID_ARG;
+  set_tile_override(cfg);
+  return I8MM_OK;
+}
+
 i8mm_status int8_quantize_weight(const void* W, int64_t N, int64_t K, int8_t* CB, float* SCB,
                                  hipStream_t stream) {
   if (N < 0 || K < 0) return I8MM_ERR_INVALID_ARG;

@@ -735,35 +735,40 @@ int cu_count() {
 }
 
 std::atomic<int64_t> g_split_override{0};
+std::atomic<int64_t> g_tile_override{-1};
 
 // Tile configurations of the wide tiles (channels x tokens per workgroup,
 // per wave, slices in flight, slice bytes per row), one workgroup per CU
 // (LDS-bound):
 //   0: 320 x 256, 8 waves of 80 x 128, two 128-byte slices (144 KB LDS)
 //   1: 256 x 256, 8 waves of 64 x 128, two 128-byte slices (128 KB LDS)
-constexpr int64_t kCfgBM[2] = {320, 256}, kCfgBN[2] = {256, 256};
+//   2: 192 x 256, 8 waves of 48 x 128, two 128-byte slices (112 KB LDS):
+//      more tiles for narrow layers (N = 5120: 216 tiles instead of 160)
+constexpr int kCfgs = 3;
+constexpr int64_t kCfgBM[kCfgs] = {320, 256, 192}, kCfgBN[kCfgs] = {256, 256, 256};
 constexpr int64_t kMaxSplits = 4;
 constexpr int64_t kMinSplitK = 1024;  // bytes of K a split walks at least
 
 // Planner: a modelled duration (microseconds) for each configuration and
-// split count, the smallest taken (ties: fewer splits, then configuration 1).
-// The workgroups run in rounds of one per CU; one walks ceil(slices / splits)
-// 128-byte slices of K at kSliceUs each, plus kItemUs of set-up and epilogue;
-// a round that fills every CU runs kFullRound times slower (the workgroups
-// share the last-level cache and fabric).  Splitting K adds the partial
-// tiles: written once per round of the split launch (kPartWriteUs a KB), read
-// back by the combine launch, whose ceil(tiles / CUs) rounds each read
-// `splits` partial tiles per CU (kPartReadUs a KB).  The constants are
-// fitted to the measured durations of both tiles on MI355X over T = 64-2048,
-// K = 4096-20480, N = 5120-20480 and 1-4 splits; the model picks the
-// fastest measured choice on all of them but one (within 0.3 %).  So the 13B
-// first feed-forward layer (20480 x 2048 outputs, K = 5120) runs 512 tiles
-// of configuration 0 in two rounds, its attention projection (5120 x 2048,
-// K = 5120) 160 tiles of configuration 1 unsplit, and the down projection
-// (5120 x 2048, K = 20480) splits K in two over 128 tiles of configuration 0.
-constexpr double kSliceUs[2] = {1.54, 1.36}, kItemUs[2] = {25.0, 20.0};
-constexpr double kFullRound[2] = {1.22, 1.085};
-constexpr double kPartWriteUs = 0.0095, kPartReadUs = 0.032;
+// split count, the smallest taken (ties: fewer splits, then the narrower
+// tile).  The workgroups run in rounds of one per CU; one walks
+// ceil(slices / splits) 128-byte slices of K at kSliceUs each, plus kItemUs
+// of set-up and epilogue; a round that fills every CU runs kFullRound times
+// slower (the workgroups share the last-level cache and fabric).  Splitting
+// K adds the partial tiles: written once per round of the split launch
+// (kPartWriteUs a KB), read back by the combine launch, whose ceil(tiles /
+// CUs) rounds each read `splits` partial tiles per CU (kPartReadUs a KB).
+// The constants are fitted to the measured durations of the three tiles on
+// MI355X over T = 64-4096, K = 4096-20480, N = 5120-49152 and 1-4 splits
+// (least squares, then tuned so that the choice is the fastest measured one:
+// it is on all but one shape, within 3.4 %).  So the 13B first
+// feed-forward layer (20480 x 2048 outputs, K = 5120) runs 512 tiles of
+// configuration 0 in two rounds, the down projection (5120 x 2048, K =
+// 20480) splits K in two over 128 of them, and the attention projection
+// (5120 x 2048, K = 5120) runs 216 tiles of configuration 2 unsplit.
+constexpr double kSliceUs[kCfgs] = {1.433, 1.415, 1.16}, kItemUs[kCfgs] = {17.8, 13.5, 11.6};
+constexpr double kFullRound[kCfgs] = {1.256, 1.101, 1.030};
+constexpr double kPartWriteUs = 0.031, kPartReadUs = 0.0289;
 
 double plan_cost(int64_t T, int64_t N, int64_t K, int c, int64_t sp, int64_t cus) {
   const int64_t tiles = ceil_div(N, kCfgBM[c]) * ceil_div(T, kCfgBN[c]);
@@ -795,7 +800,9 @@ void choose_wide(int64_t T, int64_t N, int64_t K, bool allow_split,
   for (int64_t sp = 1; sp <= kMaxSplits; ++sp) {
     if (ovr > 0 && sp != want) continue;
     if (ovr == 0 && sp > 1 && (ceil_div(K, sp) < kMinSplitK || sp > slices)) continue;
-    for (int c = 1; c >= 0; --c) {
+    const int64_t tov = g_tile_override.load();
+    for (int c = kCfgs - 1; c >= 0; --c) {
+      if (tov >= 0 && tov < kCfgs && c != tov) continue;
       const double cost = plan_cost(T, N, K, c, sp, cus);
       if (first || cost < best) {
         best = cost;
@@ -820,7 +827,7 @@ hipError_t launch_mode_z(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
   if (MODE != MODE_FUSED || a.splits < 1 || !a.part) a.splits = 1;
   int64_t cfg = a.cfg, sp = 1;
-  if (cfg < 0 || cfg > 1) {  // no plan: the best unsplit configuration
+  if (cfg < 0 || cfg >= kCfgs) {  // no plan: the best unsplit configuration
     choose_wide(a.T, a.N, a.K, false, &cfg, &sp);
     a.splits = 1;
   }
@@ -831,12 +838,17 @@ hipError_t launch_mode_z(const GemmArgs& a0, hipStream_t st) {
         e = launch_cfg<320, 256, 80, 128, 2, 128, MODE_PART>(a, st);
         return e != hipSuccess ? e : launch_cfg<320, 256, 80, 128, 2, 128, MODE_COMBINE, false, ZP>(a, st);
       }
+      if (cfg == 2) {
+        e = launch_cfg<192, 256, 48, 128, 2, 128, MODE_PART>(a, st);
+        return e != hipSuccess ? e : launch_cfg<192, 256, 48, 128, 2, 128, MODE_COMBINE, false, ZP>(a, st);
+      }
       e = launch_cfg<256, 256, 64, 128, 2, 128, MODE_PART>(a, st);
       return e != hipSuccess ? e
                              : launch_cfg<256, 256, 64, 128, 2, 128, MODE_COMBINE, false, ZP>(a, st);
     }
   }
   if (cfg == 0) return launch_cfg<320, 256, 80, 128, 2, 128, MODE, false, ZP>(a, st);
+  if (cfg == 2) return launch_cfg<192, 256, 48, 128, 2, 128, MODE, false, ZP>(a, st);
   return launch_cfg<256, 256, 64, 128, 2, 128, MODE, false, ZP>(a, st);
 }
 
@@ -850,6 +862,7 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t st) {
 }  // namespace
 
 void set_split_override(int64_t splits) { g_split_override.store(splits > 0 ? splits : 0); }
+void set_tile_override(int64_t cfg) { g_tile_override.store(cfg >= 0 && cfg < kCfgs ? cfg : -1); }
 int64_t split_override() { return g_split_override.load(); }
 
 GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K) {

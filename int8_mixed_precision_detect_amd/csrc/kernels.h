@@ -110,6 +110,8 @@ GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K);
 // and tuning control.
 void set_split_override(int64_t splits);
 int64_t split_override();
+// Process-wide choice of the wide tile configuration (-1: the plan's own).
+void set_tile_override(int64_t cfg);
 hipError_t launch_gemm_i8_fused(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_i8_s32(const GemmArgs& a, hipStream_t st);
 

@@ -208,6 +208,30 @@ def test_split_k_is_bit_identical(i8, T, K, N, planted):
         assert np.array_equal(o, outs[0])
 
 
+@pytest.mark.parametrize("T,K,N,planted", [(600, 4112, 1000, 5), (2048, 1024, 5000, 40),
+                                            (257, 520, 700, 3)])
+def test_tile_configs_are_bit_identical(i8, T, K, N, planted):
+    # the three wide tiles (320, 256, 192 channels x 256 tokens) compute each
+    # element with the same operations in the same order: Y is the same bits,
+    # unsplit and with K split in two; every one within the oracle's bound.
+    # Ragged channel and token tiles; K = 4112 ends in a partial slice.
+    d = make_random_case(T * 3 + K + N, T, K, N, n_planted=planted, bias=True)
+    outs = []
+    try:
+        for sp in (1, 2):
+            i8.set_split_override(sp)
+            for cfg in (0, 1, 2):
+                i8.set_tile_override(cfg)
+                Y, _, _ = _full_check(i8, d["X"], d["W"], d["bias"], 6.0,
+                                      f"tile {cfg} split {sp} {T}x{K}x{N}")
+                outs.append(host(Y).view(np.uint16))
+    finally:
+        i8.set_tile_override(-1)
+        i8.set_split_override(0)
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
 def test_down_projection_plans_a_split(i8):
     # 13B down projection: 128 output tiles for 256 compute units
     lay = i8.workspace_layout(2048, 5120, 20480)
