@@ -17,19 +17,33 @@ namespace i8mm {
 // ---------------------------------------------------------------------------
 // Weight quantization: one workgroup per output channel j (row of W[N,K]).
 // Pass 1 takes the row absmax (exact: the max of fp16 magnitudes), pass 2
-// re-reads the row (an L2 hit) and writes the codes.
+// writes the codes.  A thread keeps up to kWqCache 16-byte chunks of the row
+// in registers between the passes (K <= 16384), all requested at once
+// (buffer loads: chunks past the row read 0); chunks beyond are read again.
 // ---------------------------------------------------------------------------
+constexpr int kWqCache = 8;
 template <bool VEC>
 __global__ __launch_bounds__(256) void k_wquant(const _Float16* __restrict__ W, int64_t K,
                                                 int8_t* __restrict__ CB, float* __restrict__ SCB) {
+  // (buffer resources are amdgcn-only; the host pass needs the signature)
+#if defined(__HIP_DEVICE_COMPILE__)
   __shared__ float red[4];
   const int64_t j = blockIdx.x;
   const _Float16* row = W + j * K;
   int8_t* out = CB + j * K;
   float m = 0.0f;
+  v8h cache[VEC ? kWqCache : 1];
   if (VEC) {
     const int64_t nc = K / 8;
-    for (int64_t c = threadIdx.x; c < nc; c += 256) m = fmaxf(m, absmax8(*(const v8h*)(row + c * 8)));
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(row, (uint32_t)(nc * 16));
+#pragma unroll
+    for (int u = 0; u < kWqCache; ++u)
+      cache[u] = __builtin_bit_cast(
+          v8h, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)(threadIdx.x + 256 * u) * 16, 0, 0));
+#pragma unroll
+    for (int u = 0; u < kWqCache; ++u) m = fmaxf(m, absmax8(cache[u]));
+    for (int64_t c = threadIdx.x + 256 * kWqCache; c < nc; c += 256)
+      m = fmaxf(m, absmax8(*(const v8h*)(row + c * 8)));
   } else {
     for (int64_t k = threadIdx.x; k < K; k += 256) m = fmaxf(m, fabsf(h2f(row[k])));
   }
@@ -38,12 +52,18 @@ __global__ __launch_bounds__(256) void k_wquant(const _Float16* __restrict__ W, 
   if (threadIdx.x == 0) SCB[j] = s;
   if (VEC) {
     const int64_t nc = K / 8;
-    for (int64_t c = threadIdx.x; c < nc; c += 256)
+#pragma unroll
+    for (int u = 0; u < kWqCache; ++u) {
+      const int64_t c = threadIdx.x + 256 * u;
+      if (c < nc) *(v2u*)(out + c * 8) = absmax_codes8(cache[u], s, r);
+    }
+    for (int64_t c = threadIdx.x + 256 * kWqCache; c < nc; c += 256)
       *(v2u*)(out + c * 8) = absmax_codes8(*(const v8h*)(row + c * 8), s, r);
   } else {
     for (int64_t k = threadIdx.x; k < K; k += 256)
       out[k] = (int8_t)absmax_code(h2f(row[k]), s, r);
   }
+#endif
 }
 
 void launch_wquant(const _Float16* W, int64_t N, int64_t K, int8_t* CB, float* SCB, bool vec,
