@@ -163,9 +163,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       static_assert(RPP % 8 == 0, "swizzle period");
       // 32-bit arithmetic: the offset is the low 32 bits either way (a
       // buffer resource spans less than 4 GB), and 32-bit values keep
-      // fewer registers live across the K loop
-      const uint32_t g = (uint32_t)(isA ? min(m0 + rr, a.N - 1) : min(n0 + rr, a.T - 1));
-      voff[u] = g * (uint32_t)(isA ? ldab : ldbb) + (uint32_t)kc;
+      // fewer registers live across the K loop.  Rows past the operand (a
+      // ragged last tile, the token rows of a few-token tile beyond T) get
+      // an out-of-range offset: they read zeros without touching memory
+      // (their results are never stored; a clamped row made every such
+      // lane re-read one line of the last row)
+      const int64_t gr = isA ? m0 + rr : n0 + rr;
+      voff[u] = gr < (isA ? a.N : a.T)
+                    ? (uint32_t)gr * (uint32_t)(isA ? ldab : ldbb) + (uint32_t)kc
+                    : 0x80000000u;
     }
   };
   auto lds_dst = [&](int buf, int u) {
