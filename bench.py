@@ -213,6 +213,19 @@ def main() -> int:
         raise RuntimeError(f"timed {calls} calls, expected {args.steps}")
     stage_avg = [m / max(calls, 1) for m in stage_ms]
 
+    # per-call spread: the same calls once more, each bracketed by its own
+    # events on the launch stream (torch's current stream)
+    per_call = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for s, (e0, e1) in enumerate(evs):
+        e0.record()
+        step(s)
+        e1.record()
+    torch.cuda.synchronize()
+    per_call = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    pct = lambda q: round(per_call[min(len(per_call) - 1, int(q * (len(per_call) - 1) + 0.5))], 2)
+
     ops = 2.0 * T * N * K
     tops = ops / (ms_per_step * 1e-3) / 1e12
     gemm_ms = stage_avg[2]
@@ -271,6 +284,7 @@ def main() -> int:
             "detect": round(detect_bytes / (stage_avg[0] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "quantize_gather": round(quant_bytes / (stage_avg[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "pct_int8_peak_whole_call": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+        "per_call_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "calls": len(per_call)},
     }
 
     if not args.no_fp16:
