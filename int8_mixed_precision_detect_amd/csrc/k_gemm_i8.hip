@@ -585,6 +585,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
     }
     asm volatile("" : "+v"(lrow), "+v"(lcol));
     const bool yvec = ((a.N & 3) == 0) && ((((uintptr_t)a.Y) & 7) == 0);
+    const bool bvec = a.bias && ((((uintptr_t)a.bias) & 7) == 0);
     // Zero-point activations: the offset part of the int8 product,
     // (sx Z / 127) (SCB R / 127) with R the channel's kept-column code sum,
     // is a rank-1 term; it is added here in fp32, one factor per token and
@@ -629,6 +630,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
 #pragma unroll
           for (int r = 0; r < 4; ++r) bv[r] = f + r < a.N ? h2f(hv[r]) : 0.0f;
         }
+      } else if (bvec && f + 3 < a.N) {
+        // 4 consecutive channels: one 8-byte load
+        const v4h hv = *(const v4h*)(a.bias + f);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bv[r] = h2f(hv[r]);
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) bv[r] = (a.bias && f + r < a.N) ? h2f(a.bias[f + r]) : 0.0f;
