@@ -232,6 +232,30 @@ def test_tile_configs_are_bit_identical(i8, T, K, N, planted):
         assert np.array_equal(o, outs[0])
 
 
+@pytest.mark.parametrize("T,K,N", [(600, 1024, 1000), (40, 256, 64)])
+def test_bias_at_an_unaligned_address(i8, T, K, N):
+    # a bias view one element into a buffer (2-byte but not 8-byte aligned):
+    # the wide tiles then read it element by element; Y must be the same bits
+    # as with an aligned copy of the same values
+    import torch
+    d = make_random_case(T + K + N + 5, T, K, N, n_planted=3, bias=True)
+    Xd = dev(d["X"])
+    CB, SCB = i8.quantize_weight(dev(d["W"]))
+    ws = i8.alloc_workspace(T, N, K)
+    b_aligned = dev(d["bias"])
+    buf = torch.zeros(N + 1, dtype=torch.float16, device="cuda")
+    buf[1:] = b_aligned
+    b_off = buf[1:]
+    assert b_off.data_ptr() % 8 != 0
+    say("forward unaligned bias", T, K, N)
+    Y1 = host(i8.linear_forward(Xd, CB, SCB, b_aligned, 6.0, workspace=ws)).view(np.uint16)
+    Y2 = host(i8.linear_forward(Xd, CB, SCB, b_off, 6.0, workspace=ws)).view(np.uint16)
+    assert np.array_equal(Y1, Y2)
+    CBo, SCBo = O.quantize_weight(d["W"])
+    Yo = O.linear_forward(d["X"], CBo, SCBo, d["bias"], 6.0)
+    assert_y_close(Y2.view(np.float16), Yo, "unaligned bias")
+
+
 def test_down_projection_plans_a_split(i8):
     # 13B down projection: 128 output tiles for 256 compute units
     lay = i8.workspace_layout(2048, 5120, 20480)
