@@ -771,16 +771,17 @@ constexpr int64_t kMinSplitK = 1024;  // bytes of K a split walks at least
 // (kPartWriteUs a KB), read back by the combine launch, whose ceil(tiles /
 // CUs) rounds each read `splits` partial tiles per CU (kPartReadUs a KB).
 // The constants are fitted to the measured durations of the three tiles on
-// MI355X over T = 64-4096, K = 4096-20480, N = 5120-49152 and 1-4 splits
-// (least squares, then tuned so that the choice is the fastest measured one:
-// it is on all but one shape, within 3.4 %).  So the 13B first
-// feed-forward layer (20480 x 2048 outputs, K = 5120) runs 512 tiles of
-// configuration 0 in two rounds, the down projection (5120 x 2048, K =
-// 20480) splits K in two over 128 of them, and the attention projection
-// (5120 x 2048, K = 5120) runs 216 tiles of configuration 2 unsplit.
-constexpr double kSliceUs[kCfgs] = {1.433, 1.415, 1.16}, kItemUs[kCfgs] = {17.8, 13.5, 11.6};
-constexpr double kFullRound[kCfgs] = {1.256, 1.101, 1.030};
-constexpr double kPartWriteUs = 0.031, kPartReadUs = 0.0289;
+// MI355X over 21 shapes, T = 64-4096, K = 4096-20480, N = 4096-49152 and
+// 1-4 splits (least squares, then tuned so that the choice is the fastest
+// measured one: it is on 17 shapes, within 5.7 % on the other four).  So
+// the 13B first feed-forward layer (20480 x 2048 outputs, K = 5120) runs
+// 512 tiles of configuration 0 in two rounds, the down projection (5120 x
+// 2048, K = 20480) splits K in two over 128 of them, and the attention
+// projection (5120 x 2048, K = 5120) runs 216 tiles of configuration 2
+// unsplit.
+constexpr double kSliceUs[kCfgs] = {1.44, 1.45, 1.131}, kItemUs[kCfgs] = {16.44, 11.23, 10.85};
+constexpr double kFullRound[kCfgs] = {1.213, 1.123, 1.040};
+constexpr double kPartWriteUs = 0.0409, kPartReadUs = 0.0293;
 
 double plan_cost(int64_t T, int64_t N, int64_t K, int c, int64_t sp, int64_t cus) {
   const int64_t tiles = ceil_div(N, kCfgBM[c]) * ceil_div(T, kCfgBN[c]);
