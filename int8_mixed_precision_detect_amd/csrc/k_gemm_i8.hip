@@ -146,10 +146,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   // a lane's chunk within its row: rows of a piece start at multiples of
   // RPP (8 or 16), so the swizzle of row rr depends only on the lane
   const int kc = ((lane % CPR) ^ swz<KB>(lane / CPR)) * 16;
+  // The resources start at the tile's first row and span its rows only, so
+  // an operand of any size is addressed with 32-bit offsets as long as
+  // BM (BN) rows of it fit in 2^31 bytes, which the host checks.
   auto setup = [&](const char* A, int64_t ldab, int64_t rowsA, const char* B, int64_t ldbb,
                    int64_t rowsB) {
-    rsA = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)(rowsA * ldab), 0x00020000);
-    rsB = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, (int)(rowsB * ldbb), 0x00020000);
+    const int64_t ra = rowsA - m0 < BM ? rowsA - m0 : BM;
+    const int64_t rb = rowsB - n0 < BN ? rowsB - n0 : BN;
+    rsA = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * ldab), (short)0,
+                                            (int)(ra > 0 ? ra * ldab : 0), 0x00020000);
+    rsB = __builtin_amdgcn_make_buffer_rsrc((void*)(B + n0 * ldbb), (short)0,
+                                            (int)(rb > 0 ? rb * ldbb : 0), 0x00020000);
     // an opaque copy of the lane index: the row indices of a later setup
     // (the outlier operands index the same channels) are recomputed rather
     // than kept live across the K loop
@@ -161,8 +168,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       const bool isA = j < ACH;
       const int rr = (isA ? j : j - ACH) * RPP + ln / CPR;
       static_assert(RPP % 8 == 0, "swizzle period");
-      // 32-bit arithmetic: the offset is the low 32 bits either way (a
-      // buffer resource spans less than 4 GB), and 32-bit values keep
+      // 32-bit arithmetic (the offset within the tile's rows), which keeps
       // fewer registers live across the K loop.  Rows past the operand (a
       // ragged last tile, the token rows of a few-token tile beyond T) get
       // an out-of-range offset: they read zeros without touching memory
@@ -170,7 +176,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
       // lane re-read one line of the last row)
       const int64_t gr = isA ? m0 + rr : n0 + rr;
       voff[u] = gr < (isA ? a.N : a.T)
-                    ? (uint32_t)gr * (uint32_t)(isA ? ldab : ldbb) + (uint32_t)kc
+                    ? (uint32_t)rr * (uint32_t)(isA ? ldab : ldbb) + (uint32_t)kc
                     : 0x80000000u;
     }
   };
@@ -889,13 +895,14 @@ GemmPlan plan_gemm_i8(int64_t T, int64_t N, int64_t K) {
 
 bool gemm_i8_supported(const GemmArgs& a) {
   // 16-byte aligned rows and operands (Wo, Xo null for the int32 product),
-  // every operand addressable with 31-bit offsets
-  const int64_t lim = (int64_t)1 << 31;
+  // the rows of one tile (at most 512 of an operand) addressable with 31-bit
+  // offsets; the operands themselves may exceed 2^32 bytes
+  const int64_t lim = (int64_t)1 << 31, rows = 512;
   return (a.K % 16 == 0) && (a.lda % 16 == 0) && (a.ldb % 16 == 0) &&
          ((((uintptr_t)a.A) & 15) == 0) && ((((uintptr_t)a.B) & 15) == 0) &&
          ((((uintptr_t)a.Wo) & 15) == 0) && ((((uintptr_t)a.Xo) & 15) == 0) &&
-         ((a.ldo * 2) % 16 == 0) && a.N * a.lda < lim && a.T * a.ldb < lim &&
-         a.N * a.ldo * 2 < lim && a.T * a.ldo * 2 < lim;
+         ((a.ldo * 2) % 16 == 0) && rows * a.lda < lim && rows * a.ldb < lim &&
+         rows * a.ldo * 2 < lim;
 }
 
 hipError_t launch_gemm_i8_s32(const GemmArgs& a, hipStream_t st) {

@@ -448,3 +448,28 @@ def test_full_size_workload_sampled(i8, name):
     n = _sampled_check(i8, name)
     if name != "175b":
         assert n == WORKLOADS[name].n_planted
+
+
+@pytest.mark.parametrize("T", [8, 300])
+def test_weight_above_2gib(i8, T):
+    # an int8 weight of 65600 x 32768 (2.15e9 bytes, more than 2^31): the
+    # tiled product addresses each tile's rows from the tile's own base, so
+    # channels past byte 2^31 (j >= 65536) are checked with the rest
+    import torch
+    N, K = 65600, 32768
+    g = torch.Generator(device="cuda").manual_seed(77)
+    CB = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+    SCB = torch.rand(N, device="cuda", generator=g) * 0.5 + 0.01
+    rng = np.random.default_rng(T)
+    X = rng.standard_normal((T, K)).astype(np.float16)
+    X[:, [5, 20000, 32767]] = np.float16(9.0)
+    rows = np.sort(rng.choice(T, size=min(T, 24), replace=False))
+    cols = np.concatenate([np.sort(rng.choice(65536, size=160, replace=False)),
+                           np.arange(65536 - 8, N)])
+    say("forward above 2 GiB", T, K, N)
+    Y = i8.linear_forward(dev(X), CB, SCB, None, 6.0)
+    ci = torch.from_numpy(cols).cuda()
+    Ys = host(Y[torch.from_numpy(rows).cuda()][:, ci])
+    Yo, Oo = O.linear_forward_sampled(X, host(CB[ci]), host(SCB[ci]), None, 6.0, rows)
+    assert list(Oo) == [5, 20000, 32767]
+    assert_y_close(Ys, Yo, "above 2 GiB")
