@@ -110,6 +110,9 @@ def test_split_k_layout(L):
     (1024, 5120, 5120, 2),
     (256, 5120, 20480, 4),    # K-heavy, few tokens: 20 tiles
     (128, 5120, 5120, 3),     # (two splits measured 3 % faster)
+    (512, 4096, 4096, 1),     # LLaMA-like widths, one launch fastest
+    (1024, 5120, 20480, 2),   # K-heavy, 1024 tokens: two splits fastest
+    (2048, 11008, 4096, 1),
 ])
 def test_planner_choices(L, T, N, K, splits):
     # the split counts the planner's duration model picks for 256 compute
