@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define I8MM_ABI_VERSION 5
+#define I8MM_ABI_VERSION 6
 
 typedef enum {
   I8MM_OK = 0,
@@ -143,6 +143,19 @@ i8mm_status int8_linear_workspace_layout(int64_t T, int64_t N, int64_t K,
 size_t int8_linear_workspace_size(int64_t T, int64_t N, int64_t K, int64_t max_outliers);
 
 /*
+ * Make a workspace ready for the forward calls below: zero-fills its head
+ * (counts, outlier list, outlier mask; a fill kernel on `stream`, no
+ * memset).  Call it once per workspace before its first forward.  Every
+ * forward leaves the mask zero again (its product kernel clears it after
+ * step 2 has read it), which saves the next call a clearing launch.  A
+ * workspace whose forward returned an error, or that held something else
+ * meanwhile, must be initialized again.  Arguments as
+ * int8_linear_workspace_layout; ws 256-byte aligned.
+ */
+i8mm_status int8_linear_workspace_init(void* ws, int64_t T, int64_t N, int64_t K,
+                                       int64_t max_outliers, hipStream_t stream);
+
+/*
  * The layer (steps 1-3 of "LLM.int8() の核心アイデア"):
  *
  *   O      = ascending { k : exists i, |X[i,k]| >= threshold }
@@ -160,9 +173,11 @@ size_t int8_linear_workspace_size(int64_t T, int64_t N, int64_t K, int64_t max_o
  *              int8).  NaN or <= 0 -> I8MM_ERR_INVALID_ARG.
  *   Y        : fp16 [T, N] out; must not overlap X, CB or the workspace
  *   ws       : device workspace, 256-byte aligned, ws_bytes >=
- *              int8_linear_workspace_size(T, N, K, max_outliers); its
- *              regions hold the intermediate results after the call
- *              (see i8mm_ws_layout)
+ *              int8_linear_workspace_size(T, N, K, max_outliers),
+ *              initialized (int8_linear_workspace_init) before its first
+ *              forward; its regions hold the intermediate results after
+ *              the call (see i8mm_ws_layout), except the mask, which the
+ *              call leaves zero
  *   max_outliers: capacity of O, in [0, K]; K is always enough.  If the
  *              device finds more, Y is undefined and int8_linear_status
  *              returns I8MM_ERR_OUTLIER_OVERFLOW; no memory outside the

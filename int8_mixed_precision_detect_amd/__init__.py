@@ -24,7 +24,7 @@ __all__ = [
     "I8mmError", "quantize_weight", "linear_forward", "linear_forward_fp16w", "weight_rowsum",
     "linear_forward_zeropoint", "workspace_layout",
     "workspace_size",
-    "alloc_workspace", "linear_status", "find_outliers", "quantize_rows", "outlier_weights",
+    "alloc_workspace", "init_workspace", "linear_status", "find_outliers", "quantize_rows", "outlier_weights",
     "gemm_s32", "profile_enable", "profile_read", "set_split_override", "set_tile_override", "Int8Linear",
 ]
 
@@ -77,9 +77,21 @@ def workspace_size(T: int, N: int, K: int, max_outliers: Optional[int] = None) -
 
 def alloc_workspace(T: int, N: int, K: int, max_outliers: Optional[int] = None,
                     device="cuda") -> torch.Tensor:
-    """A uint8 device buffer big enough for a forward call of this shape."""
-    return torch.empty(max(workspace_size(T, N, K, max_outliers), 256), dtype=torch.uint8,
-                       device=device)
+    """A uint8 device buffer big enough for a forward call of this shape,
+    initialized (``int8_linear_workspace_init``) on the current stream."""
+    mo = K if max_outliers is None else max_outliers
+    ws = torch.empty(max(workspace_size(T, N, K, mo), 256), dtype=torch.uint8, device=device)
+    init_workspace(ws, T, N, K, mo)
+    return ws
+
+
+def init_workspace(ws: torch.Tensor, T: int, N: int, K: int,
+                   max_outliers: Optional[int] = None) -> None:
+    """Zero the head of a workspace (counts, outlier list, mask) before its
+    first forward; forwards leave it ready for the next one."""
+    mo = K if max_outliers is None else max_outliers
+    check("int8_linear_workspace_init",
+          lib().int8_linear_workspace_init(_ptr(ws), T, N, K, mo, _stream(ws)))
 
 
 def linear_forward(X: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor,

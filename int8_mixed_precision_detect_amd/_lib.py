@@ -39,6 +39,7 @@ SIGNATURES = {
     "int8_quantize_weight": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_ptr]),
     "int8_linear_workspace_layout": (c_int, [c_i64, c_i64, c_i64, c_i64, ctypes.POINTER(WsLayout)]),
     "int8_linear_workspace_size": (c_size, [c_i64, c_i64, c_i64, c_i64]),
+    "int8_linear_workspace_init": (c_int, [c_ptr, c_i64, c_i64, c_i64, c_i64, c_ptr]),
     "int8_linear_forward": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_i64, c_ptr, c_float,
                                     c_ptr, c_ptr, c_size, c_i64, c_ptr]),
     "int8_weight_rowsum": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr]),

@@ -2,6 +2,7 @@
 // kernel sequencing on the caller's stream.  See include/i8mm.h for the
 // contract of every entry point.
 #include <math.h>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -15,13 +16,12 @@ namespace {
 
 constexpr int64_t kAlign = 256;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // sizes must fit int32 indexing of O
-constexpr int64_t kMaxK = (int64_t)1 << 18;    // LDS copy of the outlier bit mask (32 KB)
 
 inline bool aligned(const void* p, uintptr_t a) { return (((uintptr_t)p) & (a - 1)) == 0; }
 
 // O-list capacity (entries) the step-2 workgroups keep in LDS; larger
 // outlier sets are enumerated from the mask instead.
-constexpr int64_t kOcap = 4096;
+constexpr int64_t kOcap = kMaxOcap;
 
 i8mm_status layout_of(int64_t T, int64_t N, int64_t K, int64_t max_o, i8mm_ws_layout* L) {
   if (T < 0 || N < 0 || K < 0 || max_o < 0 || max_o > K) return I8MM_ERR_INVALID_ARG;
@@ -59,7 +59,7 @@ i8mm_status hip_status() {
 // ---- instrumentation state ----
 constexpr int kProfCap = 4096;
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
 int g_prof_n = 0;
 std::vector<hipEvent_t> g_prof_ev;  // kProfCap * 4 events, created on first enable
 
@@ -112,6 +112,19 @@ i8mm_status int8_linear_workspace_layout(int64_t T, int64_t N, int64_t K, int64_
   return layout_of(T, N, K, max_outliers, out);
 }
 
+i8mm_status int8_linear_workspace_init(void* ws, int64_t T, int64_t N, int64_t K,
+                                       int64_t max_outliers, hipStream_t stream) {
+  i8mm_ws_layout L;
+  const i8mm_status ls = layout_of(T, N, K, max_outliers, &L);
+  if (ls != I8MM_OK) return ls;
+  if (!ws || !aligned(ws, kAlign)) return I8MM_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  // counts, outlier list and mask: the head of the workspace
+  launch_zero_words((uint32_t*)ws, (int64_t)((L.mask + (size_t)ceil_div(K > 0 ? K : 1, 32) * 4) / 4),
+                    stream);
+  return hip_status();
+}
+
 size_t int8_linear_workspace_size(int64_t T, int64_t N, int64_t K, int64_t max_outliers) {
   i8mm_ws_layout L;
   if (layout_of(T, N, K, max_outliers, &L) != I8MM_OK) return 0;
@@ -142,7 +155,7 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   char* w = (char*)ws;
   int32_t* counts = (int32_t*)(w + L.counts);
   hipEvent_t* ev = nullptr;
-  if (K > 0) {
+  if (K > 0 && g_prof_on.load(std::memory_order_relaxed)) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (g_prof_on && g_prof_n < kProfCap) ev = &g_prof_ev[(size_t)(g_prof_n++) * 4];
   }
@@ -160,7 +173,9 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   int32_t* O = (int32_t*)(w + L.outliers);
   uint32_t* mask = (uint32_t*)(w + L.mask);
   const bool xvec = (K % 8 == 0) && aligned(X, 16);
-  launch_detect((const _Float16*)X, T, K, threshold, mask, nullptr, xvec, stream);
+  // (the mask is zero: the last forward on this workspace, or its
+  // initialization, left it so)
+  launch_detect((const _Float16*)X, T, K, threshold, mask, false, xvec, stream);
   if (ev) (void)hipEventRecord(ev[1], stream);
 
   int8_t* Xq = (int8_t*)(w + L.xq);
@@ -227,6 +242,8 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   // Wo (and, zero-point, the outlier code sums) built by step 2: the
   // few-token tiles then do not rebuild Wo from CB
   a.wo_ready = W16 != nullptr || rsum != nullptr;
+  a.clear_mask = mask;
+  a.clear_words = ceil_div(K, 32);
   pa.wo_skip = fast && T <= kFewT && !a.wo_ready ? kFewOcap : -1;
   launch_prep(pa, stream);
   if (ev) (void)hipEventRecord(ev[2], stream);
@@ -297,7 +314,7 @@ i8mm_status int8_find_outliers(const void* X, int64_t T, int64_t K, float thresh
     return I8MM_ERR_INVALID_ARG;
   (void)hipGetLastError();
   const bool xvec = (K % 8 == 0) && aligned(X, 16);
-  launch_detect((const _Float16*)X, T, K, threshold, mask, nullptr, xvec, stream);
+  launch_detect((const _Float16*)X, T, K, threshold, mask, true, xvec, stream);
   launch_compact(mask, K, O, counts, max_outliers, stream);
   return hip_status();
 }

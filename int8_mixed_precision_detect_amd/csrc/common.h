@@ -195,4 +195,14 @@ __device__ __forceinline__ float block_max(float v, float* lds /* NT/64 floats *
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+// Raises a kernel's dynamic-LDS limit to `bytes` once per process, on its
+// first launch (later calls return the first call's status without a HIP
+// call); `bytes` must be the most the kernel is ever launched with.
+template <auto Kern>
+inline hipError_t lds_limit(size_t bytes) {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  return e;
+}
+
 }  // namespace i8mm

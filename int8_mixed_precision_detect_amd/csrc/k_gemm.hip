@@ -64,6 +64,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(GemmArgs a)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / NWN) * WM, wn0 = (wave % NWN) * WN;
+  // the forward's outlier mask: step 2 is done with it; zero it for the next
+  // call's detection
+  if (a.clear_mask && blockIdx.x == 0)
+    for (int64_t w = tid; w < a.clear_words; w += NT) a.clear_mask[w] = 0u;
 
   // tile order: blocks are dealt to the 8 XCDs round-robin; give each XCD a
   // contiguous run of tiles, consecutive tiles sharing one weight tile.
@@ -281,12 +285,12 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   hipError_t e;
   if (vec) {
     auto kern = k_gemm<BM, BN, WM, WN, FUSED, true>;
-    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
+    e = lds_limit<k_gemm<BM, BN, WM, WN, FUSED, true>>(LDS);
     if (e != hipSuccess) return e;
     kern<<<dim3((unsigned)ntiles), dim3(NT), LDS, st>>>(a);
   } else {
     auto kern = k_gemm<BM, BN, WM, WN, FUSED, false>;
-    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
+    e = lds_limit<k_gemm<BM, BN, WM, WN, FUSED, false>>(LDS);
     if (e != hipSuccess) return e;
     kern<<<dim3((unsigned)ntiles), dim3(NT), LDS, st>>>(a);
   }

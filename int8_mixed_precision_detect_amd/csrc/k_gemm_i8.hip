@@ -118,6 +118,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm0 = (wave / NWN) * WM, wn0 = (wave % NWN) * WN;
+  // the forward's outlier mask: step 2 is done with it; zero it for the next
+  // call's detection (the first workgroup of the call's first product launch)
+  if (a.clear_mask && blockIdx.x == 0)
+    for (int64_t w = tid; w < a.clear_words; w += (BM / WM) * (BN / WN) * 64) a.clear_mask[w] = 0u;
 
   // work items (split, tile), split-major.  Workgroups are dealt to the 8
   // XCDs round-robin; give each XCD a contiguous run of items, consecutive
@@ -736,8 +740,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   constexpr size_t LDS = (size_t)S * (BM + BN) * KB + (MODE == MODE_FUSED_X ? few_lds(BN) : 0) +
                          (kWide ? 1024 : 0);  // the no-op refills' target
   auto kern = k_gemm_i8<BM, BN, WM, WN, S, KB, MODE, NTA, ZP>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS);
+  const hipError_t e = lds_limit<k_gemm_i8<BM, BN, WM, WN, S, KB, MODE, NTA, ZP>>(LDS);
   if (e != hipSuccess) return e;
   const int64_t items = ceil_div(a.N, BM) * ceil_div(a.T, BN) * (MODE == MODE_PART ? a.splits : 1);
   kern<<<dim3((unsigned)items), dim3(NT), LDS, st>>>(a);
@@ -853,17 +856,19 @@ hipError_t launch_mode_z(const GemmArgs& a0, hipStream_t st) {
   if constexpr (MODE == MODE_FUSED) {
     if (a.splits > 1) {  // split K: partial tiles, then one combine launch
       hipError_t e;
+      GemmArgs c = a;  // (the partial launch clears the mask)
+      c.clear_mask = nullptr;
       if (cfg == 0) {
         e = launch_cfg<320, 256, 80, 128, 2, 128, MODE_PART>(a, st);
-        return e != hipSuccess ? e : launch_cfg<320, 256, 80, 128, 2, 128, MODE_COMBINE, false, ZP>(a, st);
+        return e != hipSuccess ? e : launch_cfg<320, 256, 80, 128, 2, 128, MODE_COMBINE, false, ZP>(c, st);
       }
       if (cfg == 2) {
         e = launch_cfg<192, 256, 48, 128, 2, 128, MODE_PART>(a, st);
-        return e != hipSuccess ? e : launch_cfg<192, 256, 48, 128, 2, 128, MODE_COMBINE, false, ZP>(a, st);
+        return e != hipSuccess ? e : launch_cfg<192, 256, 48, 128, 2, 128, MODE_COMBINE, false, ZP>(c, st);
       }
       e = launch_cfg<256, 256, 64, 128, 2, 128, MODE_PART>(a, st);
       return e != hipSuccess ? e
-                             : launch_cfg<256, 256, 64, 128, 2, 128, MODE_COMBINE, false, ZP>(a, st);
+                             : launch_cfg<256, 256, 64, 128, 2, 128, MODE_COMBINE, false, ZP>(c, st);
     }
   }
   if (cfg == 0) return launch_cfg<320, 256, 80, 128, 2, 128, MODE, false, ZP>(a, st);

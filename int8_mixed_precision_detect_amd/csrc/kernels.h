@@ -8,11 +8,14 @@ namespace i8mm {
 
 void launch_wquant(const _Float16* W, int64_t N, int64_t K, int8_t* CB, float* SCB, bool vec,
                    hipStream_t st);
-// Outlier detection: zero mask[ceil(K/32)] (and counts[4] when given), then
-// OR the column flags |x| >= thr of kDetectRows-row blocks into it.
-constexpr int64_t kDetectRows = 32;
-void launch_detect(const _Float16* X, int64_t T, int64_t K, float thr, uint32_t* mask,
-                   int32_t* counts, bool vec, hipStream_t st);
+// Outlier detection: OR the column flags |x| >= thr of row blocks into
+// mask[ceil(K/32)], which must be zero on entry (clear: zero it first, with
+// one more launch -- the stage entry point; the forward's mask is left zero
+// by the previous call's product kernel).
+void launch_detect(const _Float16* X, int64_t T, int64_t K, float thr, uint32_t* mask, bool clear,
+                   bool vec, hipStream_t st);
+// zero words [0, n) of p (a fill kernel: no memset node in a captured graph)
+void launch_zero_words(uint32_t* p, int64_t n, hipStream_t st);
 // mask -> ascending O (first max_o entries), counts {n_o, overflow, 0, 0}.
 void launch_compact(const uint32_t* mask, int64_t K, int32_t* O, int32_t* counts, int64_t max_o,
                     hipStream_t st);
@@ -48,7 +51,14 @@ struct PrepArgs {
 };
 // rsum[j] = sum_k CB[j, k] (int32), once per weight (zero-point layer)
 void launch_rowsum(const int8_t* CB, int64_t N, int64_t K, int32_t* rsum, hipStream_t st);
-size_t prep_lds_bytes(int64_t K, int64_t ocap);
+// LDS of the step-2 kernel: mask[KW], pref[KW + 1], O[ocap]
+constexpr size_t prep_lds_bytes(int64_t K, int64_t ocap) {
+  return (size_t)((2 * ((K + 31) / 32) + 1 + ocap) * 4);
+}
+// Largest K the forward takes (an LDS copy of its outlier bit mask, 32 KB)
+// and the largest outlier list kept in LDS.
+constexpr int64_t kMaxK = (int64_t)1 << 18;
+constexpr int64_t kMaxOcap = 4096;
 void launch_prep(const PrepArgs& p, hipStream_t st);
 void launch_fill_bias(_Float16* Y, int64_t T, int64_t N, const _Float16* bias, int32_t* counts,
                       hipStream_t st);
@@ -83,6 +93,11 @@ struct GemmArgs {
   // Wo is already in the workspace (the few-token tiles must not rebuild it
   // from CB: the fp16-weight variant takes it from W)
   bool wo_ready;
+  // the forward's outlier mask (clear_words words), zeroed by the first
+  // workgroup of the call's first product launch: step 2 has read it, and
+  // the next call's detection starts from zero
+  uint32_t* clear_mask;
+  int64_t clear_words;
   // zero-point activations (zp non-null): acc + zp[t] * (rsum[j] - osum[j])
   // is the int8 part (osum read only when there are outlier columns)
   const int32_t* zp;
