@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define I8MM_ABI_VERSION 6
+#define I8MM_ABI_VERSION 7
 
 typedef enum {
   I8MM_OK = 0,
@@ -189,6 +189,38 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K,
                                 const void* bias, float threshold, void* Y,
                                 void* ws, size_t ws_bytes, int64_t max_outliers,
                                 hipStream_t stream);
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, serving
+ * loops that forbid hipMalloc, harnesses that do): int8_linear_forward
+ * without a workspace argument.  Its workspace is a library-owned device
+ * array of I8MM_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held from the
+ * first call on that GPU until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *
+ *   X, CB, SCB, bias, threshold, Y, max_outliers, stream:
+ *            as int8_linear_forward; same kernels, so Y is bit-identical to
+ *            that call's with the same max_outliers.
+ *   status : NULL, or caller-owned device memory of 4 int32 (4-byte
+ *            aligned) that receives [outlier columns found, 1 if more than
+ *            max_outliers (Y then undefined) else 0, 0, 0] when the stream
+ *            reaches the end of the call.  The intermediate results stay in
+ *            the library's array and are not exposed.
+ *
+ * I8MM_ERR_WORKSPACE when int8_linear_workspace_size(T, N, K, max_outliers)
+ * exceeds I8MM_NOALLOC_SCRATCH_BYTES (for example T = 2048, K = 5120,
+ * N = 13824 fits up to about 1500 outlier columns).  Every call on a GPU
+ * uses that GPU's one array: calls whose execution overlaps on one GPU
+ * (other streams, other threads) race and give undefined results; calls in
+ * one stream order are safe.  Each call clears the part of the array that
+ * must start at zero (a fill kernel, not a memset).
+ */
+#define I8MM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+i8mm_status int8_linear_forward_noalloc(const void* X, int64_t T, int64_t K,
+                                        const int8_t* CB, const float* SCB, int64_t N,
+                                        const void* bias, float threshold, void* Y,
+                                        int64_t max_outliers, int32_t* status,
+                                        hipStream_t stream);
 
 /*
  * The layer with the fp16 weight kept (the pages' Linear8bitLt interface has

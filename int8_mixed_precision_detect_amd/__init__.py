@@ -18,14 +18,14 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import I8mmError, WsLayout, check, lib
+from ._lib import NOALLOC_SCRATCH_BYTES, I8mmError, WsLayout, check, lib
 
 __all__ = [
     "I8mmError", "quantize_weight", "linear_forward", "linear_forward_fp16w", "weight_rowsum",
-    "linear_forward_zeropoint", "workspace_layout",
-    "workspace_size",
-    "alloc_workspace", "init_workspace", "linear_status", "find_outliers", "quantize_rows", "outlier_weights",
-    "gemm_s32", "profile_enable", "profile_read", "set_split_override", "set_tile_override", "Int8Linear",
+    "linear_forward_zeropoint", "linear_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "workspace_layout", "workspace_size", "alloc_workspace", "init_workspace", "linear_status",
+    "find_outliers", "quantize_rows", "outlier_weights", "gemm_s32", "profile_enable",
+    "profile_read", "set_split_override", "set_tile_override", "Int8Linear",
 ]
 
 DEFAULT_THRESHOLD = 6.0
@@ -124,6 +124,46 @@ def linear_forward(X: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor,
           lib().int8_linear_forward(_ptr(X), T, K, _ptr(CB), _ptr(SCB), N, _ptr(bias),
                                     float(threshold), _ptr(out), _ptr(workspace),
                                     workspace.numel(), mo, _stream(X)))
+    return out
+
+
+def linear_forward_noalloc(X: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor,
+                           bias: Optional[torch.Tensor] = None,
+                           threshold: float = DEFAULT_THRESHOLD, max_outliers: int = 256,
+                           out: Optional[torch.Tensor] = None,
+                           status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """linear_forward on the library's per-GPU scratch array instead of a
+    workspace (int8_linear_forward_noalloc): the call allocates nothing when
+    `out` is given.  `status` (int32 [4] on the device, optional) receives
+    [outlier columns found, overflow flag, 0, 0].  Calls that overlap on one
+    GPU race; max_outliers bounds the scratch use (I8MM_ERR_WORKSPACE past
+    NOALLOC_SCRATCH_BYTES)."""
+    _need(X, "X", torch.float16, 2)
+    _need(CB, "CB", torch.int8, 2)
+    _need(SCB, "SCB", torch.float32, 1)
+    T, K = X.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K or SCB.shape[0] != N:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)} CB {tuple(CB.shape)} "
+                         f"SCB {tuple(SCB.shape)}")
+    if bias is not None:
+        _need(bias, "bias", torch.float16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias must have N elements")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=X.device)
+    else:
+        _need(out, "out", torch.float16, 2)
+        if tuple(out.shape) != (T, N):
+            raise ValueError("out must be [T, N]")
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+        if status.numel() < 4:
+            raise ValueError("status must hold 4 int32")
+    check("int8_linear_forward_noalloc",
+          lib().int8_linear_forward_noalloc(_ptr(X), T, K, _ptr(CB), _ptr(SCB), N, _ptr(bias),
+                                            float(threshold), _ptr(out), int(max_outliers),
+                                            _ptr(status), _stream(X)))
     return out
 
 

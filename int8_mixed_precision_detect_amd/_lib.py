@@ -43,6 +43,8 @@ SIGNATURES = {
     "int8_linear_forward": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_i64, c_ptr, c_float,
                                     c_ptr, c_ptr, c_size, c_i64, c_ptr]),
     "int8_weight_rowsum": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr]),
+    "int8_linear_forward_noalloc": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_i64, c_ptr,
+                                            c_float, c_ptr, c_i64, c_ptr, c_ptr]),
     "int8_linear_forward_zeropoint": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_ptr, c_i64,
                                               c_ptr, c_float, c_ptr, c_ptr, c_size, c_i64, c_ptr]),
     "int8_linear_forward_fp16w": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_i64, c_ptr, c_float,
@@ -58,6 +60,9 @@ SIGNATURES = {
     "i8mm_profile_enable": (c_int, [c_int]),
     "i8mm_profile_read": (c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
 }
+
+# I8MM_NOALLOC_SCRATCH_BYTES: the per-GPU array of the allocation-free forward
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 STATUS = {0: "I8MM_OK", 1: "I8MM_ERR_INVALID_ARG", 2: "I8MM_ERR_WORKSPACE",
           3: "I8MM_ERR_UNSUPPORTED", 4: "I8MM_ERR_HIP", 5: "I8MM_ERR_OUTLIER_OVERFLOW"}

@@ -138,7 +138,8 @@ namespace {
 i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, const float* SCB,
                          int64_t N, const void* bias, float threshold, void* Y, void* ws,
                          size_t ws_bytes, int64_t max_outliers, hipStream_t stream,
-                         const _Float16* W16, const int32_t* rsum = nullptr) {
+                         const _Float16* W16, const int32_t* rsum = nullptr,
+                         int32_t* counts_ext = nullptr, bool zero_mask = false) {
   if (isnan(threshold) || !(threshold > 0.0f)) return I8MM_ERR_INVALID_ARG;
   i8mm_ws_layout L;
   const i8mm_status ls = layout_of(T, N, K, max_outliers, &L);
@@ -153,7 +154,7 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   (void)hipGetLastError();
 
   char* w = (char*)ws;
-  int32_t* counts = (int32_t*)(w + L.counts);
+  int32_t* counts = counts_ext ? counts_ext : (int32_t*)(w + L.counts);
   hipEvent_t* ev = nullptr;
   if (K > 0 && g_prof_on.load(std::memory_order_relaxed)) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -174,7 +175,9 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   uint32_t* mask = (uint32_t*)(w + L.mask);
   const bool xvec = (K % 8 == 0) && aligned(X, 16);
   // (the mask is zero: the last forward on this workspace, or its
-  // initialization, left it so)
+  // initialization, left it so -- except in the allocation-free forward,
+  // whose shared scratch may hold another call's layout: a fill kernel)
+  if (zero_mask) launch_zero_words(mask, ceil_div(K, 32), stream);
   launch_detect((const _Float16*)X, T, K, threshold, mask, false, xvec, stream);
   if (ev) (void)hipEventRecord(ev[1], stream);
 
@@ -261,6 +264,61 @@ i8mm_status int8_linear_forward(const void* X, int64_t T, int64_t K, const int8_
                                 hipStream_t stream) {
   return forward_impl(X, T, K, CB, SCB, N, bias, threshold, Y, ws, ws_bytes, max_outliers,
                       stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free forward ----
+// Its workspace: one array per device, held from the code object's load
+// until the process ends.  Host code never uses this name as an address;
+// it takes the device address from hipGetSymbolAddress (per device).
+static __device__ __align__(256) unsigned char scratch[I8MM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, resolved on the first
+// call made with that device current.
+i8mm_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return I8MM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return I8MM_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return I8MM_ERR_HIP;
+      }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return I8MM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+i8mm_status int8_linear_forward_noalloc(const void* X, int64_t T, int64_t K, const int8_t* CB,
+                                        const float* SCB, int64_t N, const void* bias,
+                                        float threshold, void* Y, int64_t max_outliers,
+                                        int32_t* status, hipStream_t stream) {
+  i8mm_ws_layout L;
+  const i8mm_status ls = layout_of(T, N, K, max_outliers, &L);
+  if (ls != I8MM_OK) return ls;
+  if (L.total > (size_t)I8MM_NOALLOC_SCRATCH_BYTES) return I8MM_ERR_WORKSPACE;
+  if (status && !aligned(status, 4)) return I8MM_ERR_INVALID_ARG;
+  if (T == 0 || N == 0) return I8MM_OK;
+  void* ws = nullptr;
+  const i8mm_status ss = scratch_of_current_device(&ws);
+  if (ss != I8MM_OK) return ss;
+  return forward_impl(X, T, K, CB, SCB, N, bias, threshold, Y, ws, L.total, max_outliers, stream,
+                      nullptr, nullptr, status, true);
 }
 
 i8mm_status int8_weight_rowsum(const int8_t* CB, int64_t N, int64_t K, int32_t* rsum,

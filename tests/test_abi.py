@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.i8mm_abi_version() == 6
+    assert L.i8mm_abi_version() == 7
     for code, name in [(0, b"I8MM_OK"), (1, b"I8MM_ERR_INVALID_ARG"), (2, b"I8MM_ERR_WORKSPACE"),
                        (3, b"I8MM_ERR_UNSUPPORTED"), (4, b"I8MM_ERR_HIP"),
                        (5, b"I8MM_ERR_OUTLIER_OVERFLOW")]:
@@ -167,6 +167,15 @@ def test_invalid_arguments_are_rejected_on_the_host(L):
     # misaligned workspace
     assert fwd(1 << 20, 4, 8, 1 << 20, 1 << 20, 4, None, 6.0, 1 << 20, (1 << 24) + 8, need, 8,
                None) == 1
+    # the allocation-free forward: the same host checks, and a layout beyond
+    # its scratch array is refused before any HIP call
+    na = L.int8_linear_forward_noalloc
+    assert na(None, 4, 8, None, None, 4, None, 6.0, None, 9, None, None) == 1
+    assert na(None, 0, 8, None, None, 4, None, 6.0, None, 8, None, None) == 0
+    assert na(1 << 20, 2048, 5120, 1 << 20, 1 << 20, 20480, None, 6.0, 1 << 20, 5120, None,
+              None) == 2
+    assert na(1 << 20, 4, 8, 1 << 20, 1 << 20, 4, None, 6.0, 1 << 20, 8, (1 << 20) + 2,
+              None) == 1  # status not 4-byte aligned
     # too-large K for the LDS mask copy
     assert L.int8_linear_workspace_size(4, 4, (1 << 18) + 1, 0) == 0
     q = L.int8_quantize_weight
