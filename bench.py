@@ -8,11 +8,13 @@ W [20480, 5120] held as CB/SCB (quantized once, outside the timed region).
 Inputs are seeded synthetic data resident in HBM before timing starts.
 
 Prints one JSON line: effective TOPS (2*T*N*K per second over the whole
-call, from K back-to-back calls with no instrumentation), the roofline entry
-of the dominant kernel (the fused product, timed over a second run of the K
-calls by HIP events the library records around it on the same stream), the
-fp16 torch linear on the same shape for comparison, and the CPU oracle timed
-on this host's cores.
+call, from K back-to-back calls with no instrumentation, rotating over
+copies of the inputs so that the last-level cache holds none of a step's
+operands; the same K calls on one copy give the warm figure beside it), the
+roofline entry of the dominant kernel (the fused product, timed over another
+run of the K calls by HIP events the library records around it on the same
+stream), the fp16 torch linear on the same shape and copies for comparison,
+and the CPU oracle timed on this host's cores.
 """
 from __future__ import annotations
 
@@ -28,7 +30,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, 2.5 PFLOP/s
 GEMM_SOURCES = ["int8_mixed_precision_detect_amd/csrc/k_gemm_i8.hip",
+                "int8_mixed_precision_detect_amd/csrc/k_gemv.hip",
                 "int8_mixed_precision_detect_amd/csrc/common.h",
                 "int8_mixed_precision_detect_amd/csrc/kernels.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_{}_traffic.txt")  # per workload
@@ -164,7 +168,7 @@ def main() -> int:
         CBs.append(CB)
         SCBs.append(SCB)
         Ys.append(torch.empty((T, N), dtype=torch.float16, device=dev))
-        if args.layer == "fp16w":
+        if args.layer == "fp16w" or not args.no_fp16:
             Ws.append(Wd.clone())
         if args.layer == "zeropoint":
             RSs.append(i8.weight_rowsum(CB))
@@ -182,6 +186,30 @@ def main() -> int:
                                         workspace=ws, out=Ys[c])
         else:
             i8.linear_forward(Xs[c], CBs[c], SCBs[c], bias, wl.threshold, workspace=ws, out=Ys[c])
+
+    # the fp16 comparator on the same shape (torch.nn.functional.linear, i.e.
+    # hipBLASLt), rotated over the same number of input/weight copies, then on
+    # one copy; it runs before the int8 steps
+    fp16 = None
+    if not args.no_fp16:
+        F = torch.nn.functional
+        reps = max(10, args.steps // 2)
+
+        def fp16_ms(rotate):
+            for r in range(3):
+                F.linear(Xs[r % copies], Ws[r % copies], bias)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for r in range(reps):
+                c = r % copies if rotate else 0
+                F.linear(Xs[c], Ws[c], bias)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        fp16 = (fp16_ms(True), fp16_ms(False))
 
     for s in range(args.warmup):
         step(s)
@@ -201,6 +229,17 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
     ms_per_step = ms_total / args.steps
+
+    # the same K steps on copy 0 only: inputs partly held in the 256 MB
+    # last-level cache from the step before (the warm figure; `value` is the
+    # rotated one above)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(0)
+    stop.record()
+    torch.cuda.synchronize()
+    warm_ms_per_step = start.elapsed_time(stop) / args.steps
 
     # per-kernel durations: the same K steps again, with the library's HIP
     # events recorded on the launch stream around each stage (an event
@@ -235,11 +274,16 @@ def main() -> int:
     traffic = read_traffic(args.workload, args.layer)
     n_pad = -(-n_o // 32) * 32
     ldq = -(-K // 64) * 64
+    # the fp16 outlier product, the method's own work beside the int8 one
+    f16_flops = 2.0 * T * N * n_o
+    # step 2 builds the outlier weights Wo unless the few-token tiles take
+    # them from their own CB stream (int8 layer, T <= 32, n_o <= 128)
+    wo_in_prep = T > 32 or n_o > 128 or args.layer != "int8"
     if T <= 32:
         # few tokens: the product streams CB once -- an HBM-bound kernel;
         # algorithmic bytes per launch: reads CB, Xq, Xo, SCB, sx, bias;
-        # writes Y and the outlier weights Wo (picked out of the CB stream
-        # for up to 128 outlier columns, else read back from step 2's Wo)
+        # writes Y, and picks Wo out of the CB stream (writing it) when step
+        # 2 did not build it, else reads it back
         gemm_bytes = (N * K + T * ldq + 2 * T * n_pad + 4 * N + 4 * T
                       + (2 * N if d["bias"] is not None else 0) + 2 * N * n_pad + 2 * T * N)
         achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
@@ -248,23 +292,37 @@ def main() -> int:
                     "kernel": "k_gemm_i8, few-token tiles (int8 product + epilogue)",
                     "avg_ms": round(gemm_ms, 5), "algorithmic_bytes_per_launch": gemm_bytes}
     else:
+        # int8 ops against the int8 peak; the fp16 outlier flops against the
+        # fp16 peak; frac is time-weighted: the time both would take at their
+        # peaks over the measured time (the int8 ops alone when n_o is small)
         achieved = ops / (gemm_ms * 1e-3) / 1e12
+        t_min = ops / (PEAK_INT8_TOPS * 1e12) + f16_flops / (PEAK_FP16_TFLOPS * 1e12)
         splits = i8.workspace_layout(T, N, K)["splits"]
         kname = ("k_gemm_i8 (fused int8 product + epilogue)" if splits == 1 else
                  f"k_gemm_i8, K split {splits} ways (int8 partial tiles, then combine + epilogue)")
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                    "unit": "TFLOP/s", "frac": round(t_min / (gemm_ms * 1e-3), 4),
                     "traffic": traffic, "kernel": kname,
-                    "avg_ms": round(gemm_ms, 5), "algorithmic_ops_per_launch": ops}
+                    "avg_ms": round(gemm_ms, 5), "algorithmic_ops_per_launch": ops,
+                    "fp16_outlier_flops_per_launch": f16_flops,
+                    "int8_only_frac": round(achieved / PEAK_INT8_TOPS, 4)}
     detect_bytes = 2.0 * T * K
+    if args.layer == "fp16w":
+        # (the per-call weight quantization runs in the detect stage: reads
+        # W, writes CB and SCB)
+        detect_bytes += 2.0 * N * K + N * K + 4 * N
     # step-2 prep: read X, write Xq (ldq = K rounded to 64), sx and Xo; the
-    # outlier weights Wo (gather of CB[:, O], fp16 write) when it builds them
+    # outlier weights when it builds them (a gather of CB[:, O], of W[:, O]
+    # in fp16 for the fp16-weight layer, and an fp16 write); the zero-point
+    # layer's row offsets and per-channel outlier code sums
     quant_bytes = 2.0 * T * K + T * ldq + 4 * T + 2 * T * n_pad
-    if T > 32 or n_o > 128:
-        quant_bytes += N * n_o + 2 * N * n_pad
+    if wo_in_prep:
+        quant_bytes += N * n_o * (2 if args.layer == "fp16w" else 1) + 2 * N * n_pad
+    if args.layer == "zeropoint":
+        quant_bytes += 4 * T + 4 * N
 
     result = {
-        "metric": f"effective TOPS (2TNK/s) of {ENTRY[args.layer]} at T=2048; % int8 MFMA peak",
+        "metric": f"effective TOPS (2TNK/s) of {ENTRY[args.layer]} at T={T}; % int8 MFMA peak",
         "value": round(tops, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -288,27 +346,15 @@ def main() -> int:
             "quantize_gather": round(quant_bytes / (stage_avg[1] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "pct_int8_peak_whole_call": round(100.0 * tops / PEAK_INT8_TOPS, 2),
         "per_call_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "calls": len(per_call)},
+        "cold_warm_ms_per_step": {"rotated_copies": round(ms_per_step, 5),
+                                  "same_buffers": round(warm_ms_per_step, 5)},
     }
-
-    if not args.no_fp16:
-        Wh = Wd
-        Xh = Xs[0]
-        F = torch.nn.functional
-        for _ in range(5):
-            F.linear(Xh, Wh, bias)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        reps = max(10, args.steps // 2)
-        e0.record()
-        for _ in range(reps):
-            F.linear(Xh, Wh, bias)
-        e1.record()
-        torch.cuda.synchronize()
-        fp16_ms = e0.elapsed_time(e1) / reps
-        result["fp16_linear"] = {"ms": round(fp16_ms, 5),
-                                 "tflops": round(ops / (fp16_ms * 1e-3) / 1e12, 2),
-                                 "int8_over_fp16_time": round(ms_per_step / fp16_ms, 4)}
+    if fp16 is not None:
+        result["fp16_linear"] = {"ms": round(fp16[0], 5),
+                                 "tflops": round(ops / (fp16[0] * 1e-3) / 1e12, 2),
+                                 "int8_over_fp16_time": round(ms_per_step / fp16[0], 4),
+                                 "same_buffers_ms": round(fp16[1], 5),
+                                 "rotated_copies": copies}
 
     if args.copy_calib_mb > 0:
         nbytes = args.copy_calib_mb << 20

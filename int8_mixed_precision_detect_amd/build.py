@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libi8mm.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "k_prep.hip", "k_gemm.hip", "k_gemm_i8.hip"]
+SOURCES = ["api.hip", "k_prep.hip", "k_gemm.hip", "k_gemm_i8.hip", "k_gemv.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -844,6 +844,7 @@ hipError_t launch_mode_z(const GemmArgs& a0, hipStream_t st) {
   // on a CU (LDS-bound), so that the 175B-width decode shapes (N = 49152)
   // run in a single wave of workgroups.
   constexpr int FM = MODE == MODE_FUSED ? MODE_FUSED_X : MODE;
+  if (a0.T <= 4 && gemv_supported(a0)) return launch_gemv(a0, MODE == MODE_FUSED, st);
   if (a0.T <= 16) return launch_cfg<32, 16, 32, 16, 3, 128, FM, true, ZP>(a0, st);
   if (a0.T <= kFewT) return launch_cfg<64, 32, 64, 32, 3, 128, FM, true, ZP>(a0, st);
   GemmArgs a = a0;

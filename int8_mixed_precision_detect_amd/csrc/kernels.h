@@ -135,5 +135,9 @@ hipError_t launch_gemm_i8_s32(const GemmArgs& a, hipStream_t st);
 // sets of at most kFewOcap columns itself (the step-2 kernel then skips Wo).
 constexpr int64_t kFewT = 32;
 constexpr int64_t kFewOcap = 128;
+// 1 <= T <= 4: the row-streaming kernel (1 KB of a weight row per load,
+// VALU dot products)
+bool gemv_supported(const GemmArgs& a);
+hipError_t launch_gemv(const GemmArgs& a, bool fused, hipStream_t st);
 
 }  // namespace i8mm

@@ -171,6 +171,28 @@ def test_wide_outlier_sets(i8, T, K, N, thr):
     _full_check(i8, d["X"], d["W"], d["bias"], thr, f"wide set {T}x{K}x{N} thr={thr}")
 
 
+# One to four tokens: the row-streaming kernel (1 KB pieces of each weight
+# row, dot products on the lanes).  Cases: the outlier weights picked out of
+# the pieces (up to 128 columns), the fp16 pass over the workspace's Wo / Xo
+# for wider sets, N not a multiple of the 8 rows a workgroup takes, K below,
+# at and past one piece and not a multiple of it.
+@pytest.mark.parametrize("T,K,N,planted,thr", [
+    (1, 16, 37, 1, 6.0), (2, 1024, 64, 5, 6.0), (3, 1040, 70, 40, 6.0), (4, 3000, 90, 12, 6.0),
+    (1, 4096, 17, 0, 2.0), (4, 2048, 33, 0, 2.0), (2, 4096, 8, 0, float("inf")),
+])
+def test_one_to_four_tokens(i8, T, K, N, planted, thr):
+    d = make_random_case(T * 11 + K + N, T, K, N, n_planted=planted, bias=True)
+    _full_check(i8, d["X"], d["W"], d["bias"], thr, f"row-streaming {T}x{K}x{N} thr={thr}")
+
+
+@pytest.mark.parametrize("T,K,N,planted", [(1, 1040, 70, 40), (3, 2000, 45, 3), (4, 4096, 64, 12)])
+def test_one_to_four_tokens_fp16w_and_zeropoint(i8, T, K, N, planted):
+    # both layers build Wo in step 2: the row-streaming kernel's fp16 pass
+    d = make_random_case(T * 13 + K + N, T, K, N, n_planted=planted, bias=True)
+    _fp16w_check(i8, d["X"], d["W"], d["bias"], 6.0, f"fp16 weight {T}x{K}x{N}")
+    _zp_check(i8, d["X"], d["W"], d["bias"], 6.0, f"zero-point {T}x{K}x{N}")
+
+
 def test_k_zero_gives_bias(i8):
     import torch
     T, N = 5, 7

@@ -177,7 +177,10 @@ GEMM_SHAPES = [(16, 64, 64), (300, 517, 1024), (257, 300, 1000), (1, 1, 1), (5, 
                # few tokens (the thin tiles): ragged channels, K not a
                # multiple of the 128-byte slice, both tile shapes (T <= 16
                # and T <= 32)
-               (32, 1000, 4160), (17, 517, 1040), (1, 33, 16), (9, 4096, 12288), (4, 40, 0)]
+               (32, 1000, 4160), (17, 517, 1040), (1, 33, 16), (9, 4096, 12288), (4, 40, 0),
+               # one to four tokens (the row-streaming kernel): ragged rows,
+               # K past one 1 KB piece and not a multiple of it
+               (1, 1000, 3000), (2, 9, 1024), (3, 64, 2064), (4, 17, 12288)]
 
 
 @pytest.mark.parametrize("T,N,K", GEMM_SHAPES)
