@@ -256,6 +256,7 @@ void launch_compact(const uint32_t* mask, int64_t K, int32_t* O, int32_t* counts
 // LDS: mask[KW], pref[KW + 1], O[ocap].
 // ---------------------------------------------------------------------------
 constexpr int kChansPerWoBlock = 16;
+constexpr int64_t kFewChanGroups = 64;  // channel workgroups of a few-token call
 constexpr int kMaskWords = 2;  // mask words a thread requests before the row
 constexpr int kRowChunks = 4;  // 16-byte chunks of a CB row a thread streams (K <= 16384)
 // One row per workgroup measured best across the first-FF shapes (2 and 4
@@ -276,7 +277,8 @@ __global__ __launch_bounds__(256) void k_prep(
     int8_t* __restrict__ Xq, int64_t ldq, float* __restrict__ sx, _Float16* __restrict__ Xo,
     int64_t ldo, int64_t nrowblk, const int8_t* __restrict__ CB, const float* __restrict__ SCB,
     int64_t N, _Float16* __restrict__ Wo, int64_t ocap, int64_t wo_skip,
-    const _Float16* __restrict__ W16, int32_t* __restrict__ zp, int32_t* __restrict__ osum) {
+    const _Float16* __restrict__ W16, int32_t* __restrict__ zp, int32_t* __restrict__ osum,
+    int64_t nwoblk) {
   // The body uses amdgcn-only types (buffer resources); the host pass only
   // needs the kernel's signature to emit its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -499,10 +501,13 @@ __global__ __launch_bounds__(256) void k_prep(
     return;
   }
 
-  // ---- dequantized outlier weight rows, 16 channels
-  const int64_t j0 = ((int64_t)blockIdx.x - nrowblk) * kChansPerWoBlock;
+  // ---- dequantized outlier weight rows, blocks of 16 channels: block
+  // blockIdx.x - nrowblk, then every (channel workgroups)-th one after it
+  if (n_pad == 0 || n_use <= wo_skip) return;
+  for (int64_t blk = (int64_t)blockIdx.x - nrowblk; blk < nwoblk;
+       blk += (int64_t)gridDim.x - nrowblk) {
+  const int64_t j0 = blk * kChansPerWoBlock;
   const int64_t nch = min((int64_t)kChansPerWoBlock, N - j0);
-  if (n_pad == 0 || nch <= 0 || n_use <= wo_skip) return;
   if (wo_stream) {
     // Rows streamed whole: row r's 16-byte chunks go to LDS (coalesced
     // loads), the next row's loads are in flight while this one's outlier
@@ -642,6 +647,7 @@ __global__ __launch_bounds__(256) void k_prep(
       for (int64_t o = n_use + lane; o < n_pad; o += 64) worow[o] = (_Float16)0.0f;
     }
   }
+  }  // channel blocks
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -678,13 +684,18 @@ void launch_prep_t(const PrepArgs& p, dim3 g, size_t lds, int64_t nrowblk, hipSt
   (void)lds_limit<k_prep<VEC, RPB, F16W, ZP>>(prep_lds_bytes(kMaxK, kMaxOcap));
   k_prep<VEC, RPB, F16W, ZP><<<g, dim3(256), lds, st>>>(
       p.X, p.T, p.K, p.mask, p.O_out, p.counts, p.max_o, p.Xq, p.ldq, p.sx, p.Xo, p.ldo, nrowblk,
-      p.CB, p.SCB, p.N, p.Wo, p.ocap, p.wo_skip, p.W16, p.zp, p.osum);
+      p.CB, p.SCB, p.N, p.Wo, p.ocap, p.wo_skip, p.W16, p.zp, p.osum,
+      p.Wo ? ceil_div(p.N, kChansPerWoBlock) : 0);
 }
 
 void launch_prep(const PrepArgs& p, hipStream_t st) {
   constexpr int R = kRowsPerPrepBlock;
   const int64_t nrowblk = p.Xq ? ceil_div(p.T, R) : 0;
-  const int64_t nwoblk = p.Wo ? ceil_div(p.N, kChansPerWoBlock) : 0;
+  int64_t nwoblk = p.Wo ? ceil_div(p.N, kChansPerWoBlock) : 0;
+  // few tokens: the channel blocks go to a few workgroups, which usually
+  // find nothing to do (the product picks small outlier sets out of CB);
+  // launching one per block cost a few microseconds of dispatch
+  if (p.T <= kFewT && nwoblk > kFewChanGroups) nwoblk = kFewChanGroups;
   const size_t lds = prep_lds_bytes(p.K, p.ocap);
   const dim3 g((unsigned)(nrowblk + nwoblk > 0 ? nrowblk + nwoblk : 1));
   if (p.W16) {
