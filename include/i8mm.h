@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define I8MM_ABI_VERSION 7
+#define I8MM_ABI_VERSION 8
 
 typedef enum {
   I8MM_OK = 0,
@@ -107,12 +107,16 @@ i8mm_status int8_quantize_weight(const void* W, int64_t N, int64_t K,
 
 /*
  * Workspace of int8_linear_forward.  Every region starts on a 256-byte
- * boundary of `ws`; offsets are in bytes from `ws`.
+ * boundary of `ws`; offsets are in bytes from `ws`.  counts and mask come
+ * first and at the same offsets for every shape (the mask region has room
+ * for the largest K), so one workspace, initialized once, serves forwards
+ * of any shapes in turn as long as it is large enough for each.
  */
 typedef struct {
   size_t counts;   /* int32[4]: n_o (true count), overflow flag, 0, 0          */
   size_t outliers; /* int32[max_outliers]: outlier columns O, ascending       */
-  size_t mask;     /* uint32[ceil(K/32)]: bit k set iff column k is an outlier */
+  size_t mask;     /* uint32[ceil(K/32)] in use of 2^13 words: bit k set iff   */
+                   /* column k is an outlier (left zero by every forward)      */
   size_t sx;       /* fp32[T]: row scales (absmax over non-outlier columns;    */
                    /* zero-point layer: half their range, see below)           */
   size_t xq;       /* int8[T][ldq]: quantized X, outlier and pad columns 0     */
@@ -144,13 +148,15 @@ size_t int8_linear_workspace_size(int64_t T, int64_t N, int64_t K, int64_t max_o
 
 /*
  * Make a workspace ready for the forward calls below: zero-fills its head
- * (counts, outlier list, outlier mask; a fill kernel on `stream`, no
- * memset).  Call it once per workspace before its first forward.  Every
- * forward leaves the mask zero again (its product kernel clears it after
- * step 2 has read it), which saves the next call a clearing launch.  A
- * workspace whose forward returned an error, or that held something else
- * meanwhile, must be initialized again.  Arguments as
- * int8_linear_workspace_layout; ws 256-byte aligned.
+ * (counts and the whole mask region; a fill kernel on `stream`, no memset).
+ * Call it once per workspace before its first forward.  Every forward
+ * leaves the mask zero again (its product kernel clears it after step 2 has
+ * read it), which saves the next call a clearing launch, and the mask's
+ * place does not depend on the shape: forwards of other shapes may follow
+ * on the same workspace without a new initialization.  A workspace whose
+ * forward returned an error, or that held something else meanwhile, must be
+ * initialized again.  Arguments as int8_linear_workspace_layout (the shape
+ * only checks them); ws 256-byte aligned.
  */
 i8mm_status int8_linear_workspace_init(void* ws, int64_t T, int64_t N, int64_t K,
                                        int64_t max_outliers, hipStream_t stream);

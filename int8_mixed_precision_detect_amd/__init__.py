@@ -23,7 +23,8 @@ from ._lib import NOALLOC_SCRATCH_BYTES, I8mmError, WsLayout, check, lib
 __all__ = [
     "I8mmError", "quantize_weight", "linear_forward", "linear_forward_fp16w", "weight_rowsum",
     "linear_forward_zeropoint", "linear_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "workspace_layout", "workspace_size", "alloc_workspace", "init_workspace", "linear_status",
+    "workspace_layout", "workspace_size", "alloc_workspace", "init_workspace", "shared_workspace",
+    "linear_status",
     "find_outliers", "quantize_rows", "outlier_weights", "gemm_s32", "profile_enable",
     "profile_read", "set_split_override", "set_tile_override", "Int8Linear",
 ]
@@ -85,10 +86,36 @@ def alloc_workspace(T: int, N: int, K: int, max_outliers: Optional[int] = None,
     return ws
 
 
+# One workspace per (device, stream), shared by every Int8Linear: calls on
+# one stream never overlap, the mask sits at the same place for every shape
+# and forwards leave it zero, so layers of different shapes take turns on it.
+# It grows to the largest call seen and is initialized when (re)allocated.
+_SHARED_WS: dict = {}
+
+
+def shared_workspace(T: int, N: int, K: int, max_outliers: Optional[int] = None,
+                     device=None) -> torch.Tensor:
+    """The workspace of the current stream on `device`, at least large enough
+    for this shape (see ``Int8Linear``)."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    stream = torch.cuda.current_stream(device)
+    key = (device.index, stream.cuda_stream)
+    need = max(workspace_size(T, N, K, max_outliers), 256)
+    ws = _SHARED_WS.get(key)
+    if ws is None or ws.numel() < need:
+        _SHARED_WS.pop(key, None)
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            init_workspace(ws, T, N, K, max_outliers)
+        _SHARED_WS[key] = ws
+    return ws
+
+
 def init_workspace(ws: torch.Tensor, T: int, N: int, K: int,
                    max_outliers: Optional[int] = None) -> None:
-    """Zero the head of a workspace (counts, outlier list, mask) before its
-    first forward; forwards leave it ready for the next one."""
+    """Zero the head of a workspace (counts and mask) before its first
+    forward; forwards, of any shape, leave it ready for the next one."""
     mo = K if max_outliers is None else max_outliers
     check("int8_linear_workspace_init",
           lib().int8_linear_workspace_init(_ptr(ws), T, N, K, mo, _stream(ws)))
@@ -97,8 +124,14 @@ def init_workspace(ws: torch.Tensor, T: int, N: int, K: int,
 def linear_forward(X: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor,
                    bias: Optional[torch.Tensor] = None, threshold: float = DEFAULT_THRESHOLD,
                    max_outliers: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y fp16 [T,N] = the LLM.int8() product of X fp16 [T,K] with (CB, SCB), plus bias."""
+                   out: Optional[torch.Tensor] = None, check_overflow: bool = False) -> torch.Tensor:
+    """Y fp16 [T,N] = the LLM.int8() product of X fp16 [T,K] with (CB, SCB), plus bias.
+
+    max_outliers (default K, always enough) sizes the outlier list and the
+    Wo / Xo regions of the workspace.  If X has more outlier columns than
+    that, Y is undefined and the workspace's status says so
+    (``linear_status``); with ``check_overflow=True`` this call reads the
+    status (a synchronization) and raises ``I8mmError`` in that case."""
     _need(X, "X", torch.float16, 2)
     _need(CB, "CB", torch.int8, 2)
     _need(SCB, "SCB", torch.float32, 1)
@@ -124,6 +157,9 @@ def linear_forward(X: torch.Tensor, CB: torch.Tensor, SCB: torch.Tensor,
           lib().int8_linear_forward(_ptr(X), T, K, _ptr(CB), _ptr(SCB), N, _ptr(bias),
                                     float(threshold), _ptr(out), _ptr(workspace),
                                     workspace.numel(), mo, _stream(X)))
+    if check_overflow:
+        code, _ = linear_status(workspace)
+        check("int8_linear_forward", code)
     return out
 
 
@@ -357,7 +393,13 @@ class Int8Linear(torch.nn.Module):
     holds ``CB``, ``SCB`` and ``bias`` and loads back without quantizing again
     (the int8 form persists).  With ``has_fp16_weights=True`` the fp16 weight
     stays and every call quantizes it (``linear_forward_fp16w``).  Inputs are
-    fp16 ``[..., in_features]``; the product runs on the GPU only."""
+    fp16 ``[..., in_features]``; the product runs on the GPU only.
+
+    Memory: a module holds CB, SCB and bias (about half the fp16 weight);
+    the intermediate results of a call go to one workspace per (device,
+    stream) shared by all modules (``shared_workspace``), sized for the
+    largest call, with room for every column to be an outlier.  ``.half()``
+    and ``.to(dtype)`` leave CB int8 and SCB fp32."""
 
     def __init__(self, in_features: int, out_features: int, bias: bool = True,
                  has_fp16_weights: bool = False, threshold: float = DEFAULT_THRESHOLD,
@@ -378,8 +420,6 @@ class Int8Linear(torch.nn.Module):
         # the int8 form (persistent once made); scratch CB/SCB of the fp16 form
         self.register_buffer("CB", None)
         self.register_buffer("SCB", None)
-        self._ws = None
-        self._ws_key = None
         self._cb_scratch = None
         self._scb_scratch = None
 
@@ -406,8 +446,15 @@ class Int8Linear(torch.nn.Module):
         self.weight = None  # the int8 form replaces it
 
     def _apply(self, fn, recurse=True):
+        # CB (int8) and SCB (fp32) keep their dtypes under .half() / .to(dtype):
+        # they follow the module's device only (a cast would lose the scales)
+        cb, scb = self.CB, self.SCB
+        self._buffers["CB"], self._buffers["SCB"] = None, None
         super()._apply(fn, recurse)
-        self._ws, self._ws_key = None, None
+        if cb is not None:
+            dev = fn(torch.empty(0, device=cb.device)).device
+            self._buffers["CB"] = cb.to(dev)
+            self._buffers["SCB"] = scb.to(device=dev, dtype=torch.float32)
         self._cb_scratch, self._scb_scratch = None, None
         self._quantize_if_on_gpu()
         return self
@@ -443,19 +490,16 @@ class Int8Linear(torch.nn.Module):
         lead = x.shape[:-1]
         X = x.reshape(-1, self.in_features).to(torch.float16).contiguous()
         T = X.shape[0]
-        key = (T, X.device)
-        if self._ws_key != key:
-            self._ws = alloc_workspace(T, self.out_features, self.in_features, None, X.device)
-            self._ws_key = key
+        ws = shared_workspace(T, self.out_features, self.in_features, None, X.device)
         bias = None if self.bias is None else self.bias.to(torch.float16).contiguous()
         if self.has_fp16_weights:
             if self.weight is None or not self.weight.is_cuda:
                 raise RuntimeError("the fp16 weight must be on the GPU")
             Y, self._cb_scratch, self._scb_scratch = linear_forward_fp16w(
                 X, self.weight.to(torch.float16).contiguous(), bias, self.threshold,
-                workspace=self._ws, CB=self._cb_scratch, SCB=self._scb_scratch)
+                workspace=ws, CB=self._cb_scratch, SCB=self._scb_scratch)
         else:
             if self.CB is None:
                 raise RuntimeError("the weight is not quantized yet; move the module to the GPU")
-            Y = linear_forward(X, self.CB, self.SCB, bias, self.threshold, workspace=self._ws)
+            Y = linear_forward(X, self.CB, self.SCB, bias, self.threshold, workspace=ws)
         return Y.reshape(*lead, self.out_features)

@@ -15,6 +15,7 @@ using namespace i8mm;
 namespace {
 
 constexpr int64_t kAlign = 256;
+constexpr size_t kMaskRegion = (size_t)(kMaxK / 32) * 4;  // bytes: the mask of the largest K
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // sizes must fit int32 indexing of O
 
 inline bool aligned(const void* p, uintptr_t a) { return (((uintptr_t)p) & (a - 1)) == 0; }
@@ -36,8 +37,12 @@ i8mm_status layout_of(int64_t T, int64_t N, int64_t K, int64_t max_o, i8mm_ws_la
     return o;
   };
   L->counts = take(16);
+  // the mask sits at the same place, with room for the largest K, whatever
+  // the shape: forwards leave its words zero, so one initialized workspace
+  // serves calls of any shape in turn
+  L->mask = take(kMaskRegion);
   L->outliers = take((size_t)(max_o > 0 ? max_o : 1) * 4);
-  L->mask = take((size_t)(KW > 0 ? KW : 1) * 4);
+  (void)KW;
   L->sx = take((size_t)T * 4);
   L->xq = take((size_t)T * (size_t)L->ldq);
   L->xo = take((size_t)T * (size_t)L->ldo * 2);
@@ -119,9 +124,8 @@ i8mm_status int8_linear_workspace_init(void* ws, int64_t T, int64_t N, int64_t K
   if (ls != I8MM_OK) return ls;
   if (!ws || !aligned(ws, kAlign)) return I8MM_ERR_INVALID_ARG;
   (void)hipGetLastError();
-  // counts, outlier list and mask: the head of the workspace
-  launch_zero_words((uint32_t*)ws, (int64_t)((L.mask + (size_t)ceil_div(K > 0 ? K : 1, 32) * 4) / 4),
-                    stream);
+  // counts and the whole mask region: the head of the workspace
+  launch_zero_words((uint32_t*)ws, (int64_t)((L.mask + kMaskRegion) / 4), stream);
   return hip_status();
 }
 
@@ -175,8 +179,10 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   uint32_t* mask = (uint32_t*)(w + L.mask);
   const bool xvec = (K % 8 == 0) && aligned(X, 16);
   // (the mask is zero: the last forward on this workspace, or its
-  // initialization, left it so -- except in the allocation-free forward,
-  // whose shared scratch may hold another call's layout: a fill kernel)
+  // initialization, left it so.  The allocation-free forward's array has no
+  // initialization call, and a call that stopped between detection and the
+  // product would leave bits set: it clears the mask every call, a fill
+  // kernel.)
   if (zero_mask) launch_zero_words(mask, ceil_div(K, 32), stream);
   launch_detect((const _Float16*)X, T, K, threshold, mask, false, xvec, stream);
   if (ev) (void)hipEventRecord(ev[1], stream);

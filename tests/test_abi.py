@@ -1,7 +1,6 @@
 """Host-side checks of the C ABI: the library loads, exports every entry point
 include/i8mm.h declares, and rejects bad arguments before touching a GPU."""
 import ctypes
-import math
 import os
 import re
 
@@ -45,7 +44,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.i8mm_abi_version() == 7
+    assert L.i8mm_abi_version() == 8
     for code, name in [(0, b"I8MM_OK"), (1, b"I8MM_ERR_INVALID_ARG"), (2, b"I8MM_ERR_WORKSPACE"),
                        (3, b"I8MM_ERR_UNSUPPORTED"), (4, b"I8MM_ERR_HIP"),
                        (5, b"I8MM_ERR_OUTLIER_OVERFLOW")]:
@@ -59,8 +58,10 @@ def test_workspace_layout(L):
         lay = WsLayout()
         assert L.int8_linear_workspace_layout(T, N, K, mo, ctypes.byref(lay)) == 0
         assert lay.splits == 1  # these shapes fill the GPU without splitting K
-        regions = [("counts", 16), ("outliers", max(mo, 1) * 4),
-                   ("mask", max(math.ceil(K / 32), 1) * 4),
+        # counts and mask first, at fixed offsets (the mask region holds
+        # the largest K's mask)
+        assert lay.counts == 0 and lay.mask == 256
+        regions = [("counts", 16), ("mask", (1 << 18) // 8), ("outliers", max(mo, 1) * 4),
                    ("sx", T * 4), ("xq", T * lay.ldq), ("xo", T * lay.ldo * 2),
                    ("wo", N * lay.ldo * 2), ("zp", max(T, 1) * 4), ("osum", max(N, 1) * 4),
                    ("part", 0)]

@@ -472,6 +472,50 @@ def test_full_size_workload_sampled(i8, name):
         assert n == WORKLOADS[name].n_planted
 
 
+@pytest.mark.parametrize("name", ["6.7b", "13b", "13b-down", "13b-attn", "decode1", "decode8",
+                                  "decode32", "175b"])
+def test_full_size_workload_every_output(i8, name):
+    """All of Y at the workloads' full sizes against the oracle, over output
+    channel blocks (the oracle sees every row and all of X for detection);
+    CB / SCB, counts, O, sx, Xq, Xo and Wo bit for bit."""
+    import torch
+    wl = WORKLOADS[name]
+    T, K, N = wl.T, wl.K, wl.N
+    d = make_inputs(name)
+    X, W, bias, thr = d["X"], d["W"], d["bias"], d["threshold"]
+    say("forward full-size, every output", name, T, K, N)
+    Wd = dev(W)
+    CB, SCB = i8.quantize_weight(Wd)
+    del Wd
+    ws = i8.alloc_workspace(T, N, K)
+    Y = i8.linear_forward(dev(X), CB, SCB, None if bias is None else dev(bias), thr, workspace=ws)
+    Yh, CBh, SCBh = host(Y), host(CB), host(SCB)
+    del Y, CB, SCB
+    Oo = O.find_outliers(X, thr)
+    v = _ws_views(i8, ws, T, N, K, K)
+    n = len(Oo)
+    assert v["counts"][0] == n and v["counts"][1] == 0
+    assert np.array_equal(v["O"], Oo.astype(np.int32))
+    Xqo, sxo = O.quantize_rows(X, Oo)
+    assert np.array_equal(v["sx"].view(np.uint32), sxo.view(np.uint32))
+    assert np.array_equal(v["Xq"][:, :K], Xqo)
+    assert np.array_equal(v["Xo"][:, :n].view(np.uint16), X[:, Oo].view(np.uint16))
+    rows = np.arange(T)
+    worst = 0.0
+    step = 8192
+    for c0 in range(0, N, step):
+        c1 = min(N, c0 + step)
+        CBo, SCBo = O.quantize_weight(W[c0:c1])
+        assert np.array_equal(CBh[c0:c1], CBo), (name, c0)
+        assert np.array_equal(SCBh[c0:c1].view(np.uint32), SCBo.view(np.uint32)), (name, c0)
+        _, Wo = O.gather_outliers(X[:1], CBo, SCBo, Oo)
+        assert np.array_equal(v["Wo"][c0:c1, :n].view(np.uint16), Wo.view(np.uint16)), (name, c0)
+        Yo, _ = O.linear_forward_sampled(X, CBo, SCBo, None if bias is None else bias[c0:c1], thr,
+                                         rows, O=Oo)
+        worst = max(worst, assert_y_close(Yh[:, c0:c1], Yo, f"{name} channels {c0}:{c1}"))
+    print(name, "n_o", n, "max err", worst)
+
+
 @pytest.mark.parametrize("T", [8, 300])
 def test_weight_above_2gib(i8, T):
     # an int8 weight of 65600 x 32768 (2.15e9 bytes, more than 2^31): the

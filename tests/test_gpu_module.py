@@ -91,3 +91,29 @@ def test_fp16_weights_module_and_batched_input(i8):
     assert_y_close(host(Yq).reshape(10, 48),
                    O.linear_forward(X.reshape(10, 64).numpy(), CBo, SCBo,
                                     lin.bias.detach().numpy(), 6.0), "int8-form module")
+
+
+def test_modules_share_one_workspace_and_keep_scales_fp32(i8):
+    # layers of different shapes (and one decode-sized call) take turns on
+    # the stream's one workspace; after .half() the scales are still fp32
+    torch.manual_seed(5)
+    shapes = [(64, 96), (96, 40), (40, 64)]
+    lins = [torch.nn.Linear(a, b).half() for a, b in shapes]
+    mods = [i8.Int8Linear.from_linear(l).to("cuda").half() for l in lins]
+    for m in mods:
+        assert m.SCB.dtype == torch.float32 and m.CB.dtype == torch.int8
+    for rnd, T in enumerate([16, 3, 40, 1]):
+        x = torch.randn(T, 64)
+        x[:, 5] = 8.0
+        h = x.to(torch.float16)
+        for l, m in zip(lins, mods):
+            say("module chain", rnd, T, l.in_features, l.out_features)
+            y = m(h.cuda())
+            CBo, SCBo = O.quantize_weight(l.weight.detach().numpy())
+            yo = O.linear_forward(h.numpy(), CBo, SCBo, l.bias.detach().numpy(), 6.0)
+            assert_y_close(host(y), yo, f"layer {l.in_features}x{l.out_features}, T={T}")
+            h = torch.from_numpy(yo)
+    ws = i8.shared_workspace(1, 1, 1)
+    assert ws.numel() >= max(i8.workspace_size(40, b, a) for a, b in shapes)
+    assert not any(torch.is_tensor(v) and v.numel() >= ws.numel() for m in mods
+                   for v in vars(m).values())

@@ -60,3 +60,28 @@ def test_no_cpu_compute():
     m = Int8Linear(64, 32)
     with pytest.raises(RuntimeError):
         m(torch.zeros(4, 64, dtype=torch.float16))
+
+
+def test_half_keeps_the_int8_form_dtypes():
+    # .half() / .to(dtype) must not cast the scales (SCB stays fp32, CB int8)
+    CB = torch.randint(-127, 128, (32, 64), dtype=torch.int8)
+    SCB = torch.rand(32) * 3 + 0.1234567
+    m = Int8Linear(64, 32, bias=True)
+    m.load_state_dict({"CB": CB, "SCB": SCB, "bias": torch.zeros(32, dtype=torch.float16)})
+    m.half()
+    assert m.CB.dtype == torch.int8 and m.SCB.dtype == torch.float32
+    assert torch.equal(m.SCB, SCB) and torch.equal(m.CB, CB)
+    m.to(torch.float32)
+    assert m.SCB.dtype == torch.float32 and torch.equal(m.SCB, SCB)
+
+
+def test_int8_form_holds_less_than_the_fp16_weight():
+    # what a quantized module keeps between calls: CB, SCB, bias (the
+    # workspace of a call is shared by all modules of a device and stream)
+    n_out, n_in = 320, 512
+    m = Int8Linear(n_in, n_out, bias=True)
+    m.load_state_dict({"CB": torch.zeros(n_out, n_in, dtype=torch.int8),
+                       "SCB": torch.ones(n_out), "bias": torch.zeros(n_out, dtype=torch.float16)})
+    held = sum(t.numel() * t.element_size() for t in list(m.parameters()) + list(m.buffers()))
+    held += sum(v.numel() * v.element_size() for v in vars(m).values() if torch.is_tensor(v))
+    assert held < 0.6 * (2 * n_out * n_in)

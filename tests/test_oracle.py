@@ -423,9 +423,74 @@ def _m_outlier_sign(mp):
     mp.setattr(O, "outlier_matmul", lambda a, b: -good(a, b))
 
 
+# zero-point layer (reading R18 of the zenn.dev "Zeropoint Quantization"
+# section): the offset term, its column set, its sign, and 0 in the range
+
+def _zp_forward(X, CB, SCB, bias, threshold, offset_cols="kept", with_offset=True):
+    Oi = O.find_outliers(X, threshold)
+    Xq, sx, Z = O.quantize_rows_zeropoint(X, Oi)
+    Xo, Wo = O.gather_outliers(X, CB, SCB, Oi)
+    keep = np.ones(X.shape[1], dtype=bool)
+    if offset_cols == "kept":
+        keep[Oi] = False
+    R = (CB.astype(np.int64) * keep[None, :]).sum(axis=1)
+    acc = O.int8_matmul(Xq, CB)
+    if with_offset:
+        acc = acc + Z.astype(np.int64)[:, None] * R[None, :]
+    return O.aggregate(acc, sx, SCB, O.outlier_matmul(Xo, Wo), bias)
+
+
+def _m_zp_drop_offset(mp):
+    mp.setattr(O, "linear_forward_zeropoint",
+               lambda X, CB, SCB, b, t, return_stages=False: _zp_forward(X, CB, SCB, b, t,
+                                                                         with_offset=False))
+
+
+def _m_zp_offset_over_all_columns(mp):
+    mp.setattr(O, "linear_forward_zeropoint",
+               lambda X, CB, SCB, b, t, return_stages=False: _zp_forward(X, CB, SCB, b, t,
+                                                                         offset_cols="all"))
+
+
+def _m_zp_offset_sign(mp):
+    good = O.quantize_rows_zeropoint
+
+    def bad(X, Oi):
+        Xq, sx, Z = good(X, Oi)
+        return Xq, sx, -Z
+    mp.setattr(O, "quantize_rows_zeropoint", bad)
+
+
+def _m_zp_range_without_zero(mp):
+    def bad(X, Oi):
+        T, K = X.shape
+        keep = np.ones(K, dtype=bool)
+        keep[np.asarray(Oi, dtype=np.int64)] = False
+        x32 = X.astype(np.float32)
+        Xq = np.zeros((T, K), dtype=np.int8)
+        sx = np.zeros(T, dtype=np.float32)
+        Z = np.zeros(T, dtype=np.int32)
+        for i in range(T):
+            v = x32[i, keep]
+            if v.size == 0 or v.max() == v.min():
+                continue
+            a, b = np.float32(v.min()), np.float32(v.max())   # 0 not forced in
+            d = np.float32(b - a)
+            S = np.float32(np.float32(254) / d)
+            z = int(O.rhaz(np.float32(a * S))) + 127
+            t = ((x32[i] * S).astype(np.float32) - np.float32(z)).astype(np.float32)
+            Xq[i] = np.where(keep, np.clip(O.rhaz(t), -127, 127), 0).astype(np.int8)
+            sx[i] = np.float32(d / np.float32(2))
+            Z[i] = z
+        return Xq, sx, Z
+    mp.setattr(O, "quantize_rows_zeropoint", bad)
+
+
 MUTATIONS = [_m_round_half_even, _m_strict_threshold, _m_descending_outliers,
              _m_row_scale_unmasked, _m_outliers_not_zeroed, _m_drop_bias, _m_scale_127,
-             _m_wo_no_scale, _m_untransposed_gemm, _m_weight_per_column, _m_outlier_sign]
+             _m_wo_no_scale, _m_untransposed_gemm, _m_weight_per_column, _m_outlier_sign,
+             _m_zp_drop_offset, _m_zp_offset_over_all_columns, _m_zp_offset_sign,
+             _m_zp_range_without_zero]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
