@@ -66,8 +66,63 @@ __global__ __launch_bounds__(256) void k_wquant(const _Float16* __restrict__ W, 
 #endif
 }
 
+// One wave per row (16-byte aligned rows of up to 64 * 8 * CPL values): the
+// whole row in registers (lane l holds chunks l, l + 64, ...: each load
+// instruction reads 1 KB of the row), the absmax across the wave with no
+// barrier, codes written 512 bytes an instruction.  A 256-thread workgroup
+// per row spent its time in the block reduction's barriers and in its
+// dependent load-reduce-store chain: 20480 x 5120 took 70 us (4.5 TB/s of
+// reads and writes), 16384 x 4096 58 us; one wave per row with exactly the
+// row's chunks in registers: 54 us (5.8 TB/s, 72 % of HBM) and 42 us.
+template <int CPL>
+__global__ __launch_bounds__(256) void k_wquant_rows(const _Float16* __restrict__ W, int64_t N,
+                                                     int64_t K, int8_t* __restrict__ CB,
+                                                     float* __restrict__ SCB) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int lane = threadIdx.x & 63;
+  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= N) return;  // (wave-uniform)
+  const int64_t nc = K / 8;
+  const __amdgpu_buffer_rsrc_t rr = make_rsrc(W + j * K, (uint32_t)(nc * 16));
+  v8h c[CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u)
+    c[u] = __builtin_bit_cast(
+        v8h, __builtin_amdgcn_raw_buffer_load_b128(rr, (lane + 64 * u) * 16, 0, 2));
+  float m = 0.0f;
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) m = fmaxf(m, absmax8(c[u]));
+  const float s = wave_max(m);
+  const float r = code_recip(s);
+  if (lane == 0) SCB[j] = s;
+  int8_t* out = CB + j * K;
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    const int64_t ci = lane + 64 * u;
+    if (ci < nc) *(v2u*)(out + ci * 8) = absmax_codes8(c[u], s, r);
+  }
+#endif
+}
+
+template <int CPL>
+bool launch_wquant_rows(const _Float16* W, int64_t N, int64_t K, int8_t* CB, float* SCB,
+                        hipStream_t st) {
+  if (ceil_div(K / 8, 64) > CPL) return false;
+  k_wquant_rows<CPL><<<dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st>>>(W, N, K, CB, SCB);
+  return true;
+}
+
 void launch_wquant(const _Float16* W, int64_t N, int64_t K, int8_t* CB, float* SCB, bool vec,
                    hipStream_t st) {
+  // (rows longer than 12288 values: the workgroup-per-row kernel, whose
+  // registers do not grow with K, measured faster -- K = 20480: 64 against
+  // 69 us)
+  if (vec && (launch_wquant_rows<8>(W, N, K, CB, SCB, st) ||
+              launch_wquant_rows<10>(W, N, K, CB, SCB, st) ||
+              launch_wquant_rows<12>(W, N, K, CB, SCB, st) ||
+              launch_wquant_rows<16>(W, N, K, CB, SCB, st) ||
+              launch_wquant_rows<24>(W, N, K, CB, SCB, st)))
+    return;
   if (vec)
     k_wquant<true><<<dim3((unsigned)N), dim3(256), 0, st>>>(W, K, CB, SCB);
   else
