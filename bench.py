@@ -31,16 +31,21 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
 PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, 2.5 PFLOP/s
-GEMM_SOURCES = ["int8_mixed_precision_detect_amd/csrc/k_gemm_i8.hip",
-                "int8_mixed_precision_detect_amd/csrc/k_gemv.hip",
-                "int8_mixed_precision_detect_amd/csrc/common.h",
-                "int8_mixed_precision_detect_amd/csrc/kernels.h"]
+CSRC = "int8_mixed_precision_detect_amd/csrc/"
+# the sources of the product kernel that runs for T tokens (T <= 4: the
+# row-streaming one; else the tiled one)
+GEMM_SOURCES = {"gemv": [CSRC + "k_gemv.hip", CSRC + "common.h", CSRC + "kernels.h"],
+                "tiled": [CSRC + "k_gemm_i8.hip", CSRC + "common.h", CSRC + "kernels.h"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_{}_traffic.txt")  # per workload
 
 
-def kernel_fingerprint() -> str:
+def product_path(T: int) -> str:
+    return "gemv" if T <= 4 else "tiled"
+
+
+def kernel_fingerprint(path: str = "tiled") -> str:
     h = hashlib.sha256()
-    for p in GEMM_SOURCES:
+    for p in GEMM_SOURCES[path]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -66,9 +71,10 @@ def profile_tag(workload: str, layer: str) -> str:
     return workload if layer == "int8" else f"{workload}-{layer}"
 
 
-def read_traffic(workload: str, layer: str = "int8"):
+def read_traffic(workload: str, layer: str = "int8", T: int = 2048):
     """HBM bytes per launch of the product kernel from the committed counter
-    summary, or None when it is missing or was taken on other kernel source."""
+    summary, or None when it is missing or was taken on other kernel source
+    (T picks the kernel whose sources are hashed)."""
     tag = profile_tag(workload, layer)
     path = TRAFFIC_FILE.format(tag)
     if not os.path.exists(path):
@@ -79,7 +85,7 @@ def read_traffic(workload: str, layer: str = "int8"):
             if ":" in line and not line.startswith("#"):
                 k, _, v = line.partition(":")
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_fingerprint") != kernel_fingerprint() or kv.get("workload") != tag:
+    if kv.get("kernel_fingerprint") != kernel_fingerprint(product_path(T)) or kv.get("workload") != tag:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -271,7 +277,7 @@ def main() -> int:
     ops = 2.0 * T * N * K
     tops = ops / (ms_per_step * 1e-3) / 1e12
     gemm_ms = stage_avg[2]
-    traffic = read_traffic(args.workload, args.layer)
+    traffic = read_traffic(args.workload, args.layer, T)
     n_pad = -(-n_o // 32) * 32
     ldq = -(-K // 64) * 64
     # the fp16 outlier product, the method's own work beside the int8 one
@@ -289,7 +295,8 @@ def main() -> int:
         achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                    "kernel": "k_gemm_i8, few-token tiles (int8 product + epilogue)",
+                    "kernel": ("k_gemv, row-streaming (int8 product + epilogue)" if T <= 4 else
+                               "k_gemm_i8, few-token tiles (int8 product + epilogue)"),
                     "avg_ms": round(gemm_ms, 5), "algorithmic_bytes_per_launch": gemm_bytes}
     else:
         # int8 ops against the int8 peak; the fp16 outlier flops against the

@@ -141,17 +141,24 @@ __global__ __launch_bounds__(64) void k_gemv(GemmArgs a) {
     const int64_t n_o = a.counts[0];
     n_use = n_o < a.max_o ? n_o : a.max_o;
     inloop = n_use <= kFewOcap && !a.wo_ready;
-    if (inloop) {
-      for (int64_t o = lane; o < n_use; o += 64) {
-        sO[o] = a.O[o];
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-          sXo[o * TT + t] = t < a.T ? a.Xo[t * a.ldo + o] : (_Float16)0.0f;
-      }
-      __syncthreads();
-      if (n_use > 0) nextc = __builtin_amdgcn_readfirstlane(sO[0]);
-    }
   }
+  // the outlier list and the tile's X[:, O] values to LDS: run once the
+  // first pieces are in flight (done before them, its loads held every
+  // workgroup's stream back by a load latency: about 10 us a call at T = 1)
+  auto stage_outliers = [&]() {
+    if constexpr (FUSED) {
+      if (inloop) {
+        for (int64_t o = lane; o < n_use; o += 64) {
+          sO[o] = a.O[o];
+#pragma unroll
+          for (int t = 0; t < TT; ++t)
+            sXo[o * TT + t] = t < a.T ? a.Xo[t * a.ldo + o] : (_Float16)0.0f;
+        }
+        __syncthreads();
+        if (n_use > 0) nextc = __builtin_amdgcn_readfirstlane(sO[0]);
+      }
+    }
+  };
   // the codes of the outlier columns in int8 piece p (weights w): the lane
   // holding column o copies its byte of each of the R rows to sC[idx][.]
   auto extract = [&](const v4i (&w)[R], int64_t p) {
@@ -176,13 +183,14 @@ __global__ __launch_bounds__(64) void k_gemv(GemmArgs a) {
   // scheduling barriers keep the loads in this order: the compiler's own
   // waits then follow the ring (with the loads moved, it waits for them
   // all at each use). ----
-  auto run = [&](auto f16, int64_t Kb, auto& acc) {
+  auto run = [&](auto f16, int64_t Kb, auto& acc, auto&& primed) {
     const int64_t P = Kb > 0 ? ceil_div(Kb, kGvPiece) : 1;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       issue(d, d, Kb);
       __builtin_amdgcn_sched_barrier(0);
     }
+    primed();
     for (int64_t p0 = 0; p0 < P; p0 += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
@@ -222,7 +230,7 @@ __global__ __launch_bounds__(64) void k_gemv(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0;
   setup(a.A, a.lda, a.B, a.ldb);
-  run(std::false_type{}, a.K, acc);
+  run(std::false_type{}, a.K, acc, stage_outliers);
   butterfly<V>(acc, lane);
 
   // this lane's (channel row, token); the 64 / V lanes of a group agree
@@ -260,7 +268,7 @@ __global__ __launch_bounds__(64) void k_gemv(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < V; ++i) pf[i] = 0.0f;
       setup(a.Wo, a.ldo * 2, a.Xo, a.ldo * 2);
-      run(std::true_type{}, npad * 2, pf);
+      run(std::true_type{}, npad * 2, pf, [] {});
       butterfly<V>(pf, lane);
       y += pf[0];
     }

@@ -750,7 +750,9 @@ void launch_prep(const PrepArgs& p, hipStream_t st) {
   // few tokens: the channel blocks go to a few workgroups, which usually
   // find nothing to do (the product picks small outlier sets out of CB);
   // launching one per block cost a few microseconds of dispatch
-  if (p.T <= kFewT && nwoblk > kFewChanGroups) nwoblk = kFewChanGroups;
+  // (only where the product can take the outliers itself: the fp16-weight
+  // and zero-point layers always need Wo, and osum, from all blocks)
+  if (p.T <= kFewT && p.wo_skip >= 0 && nwoblk > kFewChanGroups) nwoblk = kFewChanGroups;
   const size_t lds = prep_lds_bytes(p.K, p.ocap);
   const dim3 g((unsigned)(nrowblk + nwoblk > 0 ? nrowblk + nwoblk : 1));
   if (p.W16) {

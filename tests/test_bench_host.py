@@ -26,7 +26,7 @@ def test_profile_tag(wl, layer, tag):
 
 
 def test_traffic_is_read_only_for_matching_kernel_source(tmp_path, monkeypatch):
-    fp = bench.kernel_fingerprint()
+    fp = bench.kernel_fingerprint("tiled")
     p = tmp_path / "k_gemm_{}_traffic.txt"
     (tmp_path / "k_gemm_w_traffic.txt").write_text(
         f"# comment: 1\nkernel_fingerprint: {fp}\nworkload: w\nhbm_bytes_per_launch: 1234\n")
@@ -39,6 +39,12 @@ def test_traffic_is_read_only_for_matching_kernel_source(tmp_path, monkeypatch):
     assert bench.read_traffic("v") is None          # taken on other kernel source
     assert bench.read_traffic("u") is None          # summary of another workload
     assert bench.read_traffic("missing") is None
+    # a few-token workload's summary is keyed to the row-streaming kernel
+    (tmp_path / "k_gemm_d_traffic.txt").write_text(
+        f"kernel_fingerprint: {bench.kernel_fingerprint('gemv')}\nworkload: d\n"
+        "hbm_bytes_per_launch: 7\n")
+    assert bench.read_traffic("d", T=1) == 7.0
+    assert bench.read_traffic("d", T=2048) is None
 
 
 def test_committed_summaries_parse():
