@@ -26,7 +26,8 @@ __all__ = [
     "workspace_layout", "workspace_size", "alloc_workspace", "init_workspace", "shared_workspace",
     "linear_status",
     "find_outliers", "quantize_rows", "outlier_weights", "gemm_s32", "profile_enable",
-    "profile_read", "set_split_override", "set_tile_override", "Int8Linear",
+    "profile_read", "set_split_override", "set_tile_override", "set_row_prep",
+    "Int8Linear",
 ]
 
 DEFAULT_THRESHOLD = 6.0
@@ -360,6 +361,14 @@ def set_tile_override(cfg: int = -1) -> None:
     2: 192 x 256); -1 = the library's choice.  Process-wide; size workspaces
     under the same setting."""
     check("i8mm_set_tile_override", lib().i8mm_set_tile_override(int(cfg)))
+
+
+def set_row_prep(enable: bool = True) -> None:
+    """One-token forwards of the absmax layer take steps 1-2 from one launch
+    of one workgroup (the default) or from the detection and step-2 launches.
+    Process-wide; the workspace holds the same values either way, and Y too
+    for outlier sets of up to 128 columns."""
+    check("i8mm_set_row_prep", lib().i8mm_set_row_prep(1 if enable else 0))
 
 
 def set_split_override(splits: int = 0) -> None:

@@ -36,6 +36,7 @@ SIGNATURES = {
     "i8mm_abi_version": (c_int, []),
     "i8mm_set_split_override": (c_int, [c_i64]),
     "i8mm_set_tile_override": (c_int, [c_i64]),
+    "i8mm_set_row_prep": (c_int, [c_int]),
     "int8_quantize_weight": (c_int, [c_ptr, c_i64, c_i64, c_ptr, c_ptr, c_ptr]),
     "int8_linear_workspace_layout": (c_int, [c_i64, c_i64, c_i64, c_i64, ctypes.POINTER(WsLayout)]),
     "int8_linear_workspace_size": (c_size, [c_i64, c_i64, c_i64, c_i64]),

@@ -68,6 +68,10 @@ std::atomic<bool> g_prof_on{false};
 int g_prof_n = 0;
 std::vector<hipEvent_t> g_prof_ev;  // kProfCap * 4 events, created on first enable
 
+// one-token forwards with steps 1-2 in one launch of one workgroup (see
+// i8mm_set_row_prep); a test and tuning control
+std::atomic<bool> g_row_prep{true};
+
 }  // namespace
 
 extern "C" {
@@ -89,6 +93,12 @@ int i8mm_abi_version(void) { return I8MM_ABI_VERSION; }
 i8mm_status i8mm_set_split_override(int64_t splits) {
   if (splits < 0) return I8MM_ERR_INVALID_ARG;
   set_split_override(splits);
+  return I8MM_OK;
+}
+
+i8mm_status i8mm_set_row_prep(int enable) {
+  if (enable != 0 && enable != 1) return I8MM_ERR_INVALID_ARG;
+  g_row_prep.store(enable == 1);
   return I8MM_OK;
 }
 
@@ -178,14 +188,6 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   int32_t* O = (int32_t*)(w + L.outliers);
   uint32_t* mask = (uint32_t*)(w + L.mask);
   const bool xvec = (K % 8 == 0) && aligned(X, 16);
-  // (the mask is zero: the last forward on this workspace, or its
-  // initialization, left it so.  The allocation-free forward's array has no
-  // initialization call, and a call that stopped between detection and the
-  // product would leave bits set: it clears the mask every call, a fill
-  // kernel.)
-  if (zero_mask) launch_zero_words(mask, ceil_div(K, 32), stream);
-  launch_detect((const _Float16*)X, T, K, threshold, mask, false, xvec, stream);
-  if (ev) (void)hipEventRecord(ev[1], stream);
 
   int8_t* Xq = (int8_t*)(w + L.xq);
   float* sx = (float*)(w + L.sx);
@@ -251,6 +253,30 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   // Wo (and, zero-point, the outlier code sums) built by step 2: the
   // few-token tiles then do not rebuild Wo from CB
   a.wo_ready = W16 != nullptr || rsum != nullptr;
+  // One token, absmax layer, row-streaming product: steps 1-2 are one row,
+  // done by one workgroup in one launch (k_row1: no mask, no detection
+  // launch), and the product gathers the codes of wide outlier sets itself.
+  // (In the stage profile, the detection stage covers both steps.)
+  if (T == 1 && xvec && K <= kRow1MaxK && fast && !a.wo_ready && gemv_supported(a) &&
+      g_row_prep.load(std::memory_order_relaxed)) {
+    launch_row1((const _Float16*)X, K, threshold, O, counts, max_outliers, Xq, L.ldq, sx, Xo,
+                stream);
+    if (ev) (void)hipEventRecord(ev[1], stream);
+    if (ev) (void)hipEventRecord(ev[2], stream);
+    a.wo_gather = true;
+    const hipError_t ge = launch_gemm_i8_fused(a, stream);
+    if (ge != hipSuccess) return I8MM_ERR_HIP;
+    if (ev) (void)hipEventRecord(ev[3], stream);
+    return hip_status();
+  }
+  // (the mask is zero: the last forward on this workspace, or its
+  // initialization, left it so.  The allocation-free forward's array has no
+  // initialization call, and a call that stopped between detection and the
+  // product would leave bits set: it clears the mask every call, a fill
+  // kernel.)
+  if (zero_mask) launch_zero_words(mask, ceil_div(K, 32), stream);
+  launch_detect((const _Float16*)X, T, K, threshold, mask, false, xvec, stream);
+  if (ev) (void)hipEventRecord(ev[1], stream);
   a.clear_mask = mask;
   a.clear_words = ceil_div(K, 32);
   pa.wo_skip = fast && T <= kFewT && !a.wo_ready ? kFewOcap : -1;

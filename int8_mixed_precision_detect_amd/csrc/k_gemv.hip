@@ -28,7 +28,10 @@
 // the codes give Wo (dequantized, written to the workspace) and the fp16
 // products sum_o X[t, o] Wo[j, o] in fp32, in increasing o.  Wider sets,
 // and the layers whose step 2 already built Wo, stream Wo and Xo through
-// the same loop with fp16 dot products instead.
+// the same loop with fp16 dot products instead -- except one-token calls
+// whose steps 1-2 ran as k_row1, which builds no Wo: their codes are
+// gathered from CB after the loop, 128 columns at a time, and summed the
+// same way as the extracted ones.
 //
 // Measured at 49152 x 12288 (HIP events around the product): 109 us at
 // T = 1 and 116 us at T = 4 against 124 us for the tiled few-token kernel;
@@ -246,21 +249,42 @@ __global__ __launch_bounds__(64) void k_gemv(GemmArgs a) {
     const float sj = valid ? a.SCB[f] : 0.0f;
     float y = (float)acc[0] * (sxt * (sj * (1.0f / 16129.0f)));
     const int64_t npad = round_up(n_use, 32);
-    if (inloop) {
+    // wider sets whose Wo no step-2 kernel built (wo_gather, one token):
+    // their codes are gathered from CB, kFewOcap columns at a time, and go
+    // the same way
+    const bool gather = FUSED && TT == 1 && a.wo_gather && !inloop && n_use > 0;
+    if (inloop || gather) {
       // Wo rows of this tile (zeros up to the 32-column pad), and the fp16
       // products in increasing o
-      for (int64_t i = lane; i < R * npad; i += 64) {
-        const int rr = (int)(i / npad);
-        const int64_t o = i % npad;
-        if (rr < ra) {
-          const _Float16 v = o < n_use ? dequant_weight(sC[o * R + rr], a.SCB[m0 + rr])
-                                       : (_Float16)0.0f;
-          ((_Float16*)a.Wo)[(m0 + rr) * a.ldo + o] = v;
-        }
-      }
       float px = 0.0f;
-      for (int64_t o = 0; o < n_use; ++o)
-        px += (float)sXo[o * TT + t] * (float)dequant_weight(sC[o * R + r], sj);
+      for (int64_t o0 = 0; o0 < npad; o0 += kFewOcap) {
+        const int64_t cnt = npad - o0 < kFewOcap ? npad - o0 : kFewOcap;
+        if (gather) {
+          __syncthreads();  // done with the previous columns
+          for (int64_t o = lane; o < cnt && o0 + o < n_use; o += 64) {
+            const int col = a.O[o0 + o];
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt)
+              sXo[o * TT + tt] = tt < a.T ? a.Xo[tt * a.ldo + o0 + o] : (_Float16)0.0f;
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) sC[o * R + rr] = rr < ra ? a.A[(m0 + rr) * a.lda + col] : 0;
+          }
+          __syncthreads();
+        }
+        const int64_t cb = inloop ? o0 : 0;  // first column of the chunk in sC / sXo
+        for (int64_t i = lane; i < R * cnt; i += 64) {
+          const int rr = (int)(i / cnt);
+          const int64_t o = i % cnt;
+          if (rr < ra) {
+            const _Float16 v = o0 + o < n_use
+                                   ? dequant_weight(sC[(cb + o) * R + rr], a.SCB[m0 + rr])
+                                   : (_Float16)0.0f;
+            ((_Float16*)a.Wo)[(m0 + rr) * a.ldo + o0 + o] = v;
+          }
+        }
+        for (int64_t o = 0; o < cnt && o0 + o < n_use; ++o)
+          px += (float)sXo[(cb + o) * TT + t] * (float)dequant_weight(sC[(cb + o) * R + r], sj);
+      }
       y += px;
     } else if (npad > 0) {
       // wide outlier sets, or Wo built by step 2: fp16 rows of the workspace

@@ -5,6 +5,7 @@
 //   k_compact   mask -> ascending outlier list O and counts (stage entry)
 //   k_prep      outlier list from the mask, masked row absmax, int8 codes,
 //               X[:,O] gather, dequantized weight rows CB[:,O]*SCB/127
+//   k_row1      steps 1-2 of a single row (one-token calls) in one launch
 //
 // The method: Hugging Face LLM.int8() summary (agentlenshq.com), section
 // "LLM.int8() の核心アイデア" steps 1-2; absmax rule from its section
@@ -783,6 +784,120 @@ __global__ void k_fill_bias(_Float16* Y, int64_t T, int64_t N, const _Float16* b
 void launch_fill_bias(_Float16* Y, int64_t T, int64_t N, const _Float16* bias, int32_t* counts,
                       hipStream_t st) {
   k_fill_bias<<<dim3((unsigned)ceil_div(T * N, 256)), dim3(256), 0, st>>>(Y, T, N, bias, counts);
+}
+
+// ---------------------------------------------------------------------------
+// Steps 1-2 for a single row of X (one-token calls) in one launch of one
+// workgroup: thread i holds chunks i + NT u (8 columns each) of the row in
+// registers, all requested at once.  With one row a column is an outlier
+// when its own |x| >= thr, so detection needs no mask: the flags, the
+// absmax over the other columns, the codes, the ascending list O (an
+// exclusive scan of the per-chunk counts in column order, one block-wide
+// scan per chunk round, skipped for rounds without outliers) and X[0, O]
+// are the values k_detect and k_prep produce for T = 1.  (One wave doing
+// it all took 21 us between events: its dependent VALU chains had nothing
+// to hide behind.)
+// ---------------------------------------------------------------------------
+constexpr int kRow1Threads = 512;
+constexpr int kRow1Chunks = (int)(kRow1MaxK / 8 / kRow1Threads);  // chunks a thread, at most
+
+__global__ __launch_bounds__(kRow1Threads) void k_row1(
+    const _Float16* __restrict__ X, int64_t K, float thr, int32_t* __restrict__ O,
+    int32_t* __restrict__ counts, int64_t max_o, int8_t* __restrict__ Xq, int64_t ldq,
+    float* __restrict__ sx, _Float16* __restrict__ Xo_) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NT = kRow1Threads, NW = NT / 64;
+  __shared__ float red[NW];
+  __shared__ int32_t wtot[kRow1Chunks][NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nc = K / 8;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)(K * 2));
+  v8h cv[kRow1Chunks];  // chunks past the row read 0
+#pragma unroll
+  for (int u = 0; u < kRow1Chunks; ++u)
+    cv[u] = __builtin_bit_cast(
+        v8h, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(tid + NT * u) * 16, 0, 0));
+
+  // flags and the absmax over the other columns; per round, the outlier
+  // count of each wave (for the scan)
+  uint32_t f[kRow1Chunks];
+  int incl[kRow1Chunks];
+  float m = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kRow1Chunks; ++u) {
+    uint32_t fu = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fu |= (uint32_t)(fabsf(h2f(cv[u][e])) >= thr) << e;
+    f[u] = fu;
+    m = fmaxf(m, absmax8(zero_masked8(cv[u], fu)));
+    const int cnt = __popc(fu);
+    incl[u] = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl[u], o, 64);
+      if (lane >= o) incl[u] += t;
+    }
+    if (lane == 63) wtot[u][wave] = incl[u];
+  }
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  float s = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) s = fmaxf(s, red[w]);
+  const float rs = code_recip(s);
+
+  // O (first max_o entries) and X[0, O]: columns in order are round-major
+  uint16_t* Xo = reinterpret_cast<uint16_t*>(Xo_);
+  int n_o = 0;
+#pragma unroll
+  for (int u = 0; u < kRow1Chunks; ++u) {
+    int before = 0, total = 0;  // outliers of this round in lower waves, in all
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int t = wtot[u][w];
+      before += w < wave ? t : 0;
+      total += t;
+    }
+    if (f[u]) {
+      const v4u xw = __builtin_bit_cast(v4u, cv[u]);
+      const uint32_t w0 = xw[0], w1 = xw[1], w2 = xw[2], w3 = xw[3];
+      int pos = n_o + before + incl[u] - __popc(f[u]);
+      for (uint32_t ff = f[u]; ff; ff &= ff - 1, ++pos) {
+        const int e = __builtin_ctz(ff);
+        if (pos < max_o) {
+          const uint32_t wd = e < 2 ? w0 : e < 4 ? w1 : e < 6 ? w2 : w3;
+          O[pos] = (int32_t)((tid + NT * u) * 8 + e);
+          Xo[pos] = (uint16_t)(wd >> (16 * (e & 1)));
+        }
+      }
+    }
+    n_o += total;
+  }
+  const int64_t n_use = n_o < max_o ? n_o : max_o;
+  for (int64_t o = n_use + tid; o < round_up(n_use, 32); o += NT) Xo[o] = 0;
+
+  // codes, zeros on the outlier columns and past K
+#pragma unroll
+  for (int u = 0; u < kRow1Chunks; ++u) {
+    const int64_t c = tid + NT * u;
+    if (c < nc) *(v2u*)(Xq + c * 8) = absmax_codes8(zero_masked8(cv[u], f[u]), s, rs);
+  }
+  for (int64_t k = K + 8 * tid; k < ldq; k += 8 * NT) *(v2u*)(Xq + k) = v2u{0u, 0u};
+  if (tid == 0) {
+    sx[0] = s;
+    counts[0] = n_o;
+    counts[1] = n_o > max_o ? 1 : 0;
+    counts[2] = 0;
+    counts[3] = 0;
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+void launch_row1(const _Float16* X, int64_t K, float thr, int32_t* O, int32_t* counts,
+                 int64_t max_o, int8_t* Xq, int64_t ldq, float* sx, _Float16* Xo,
+                 hipStream_t st) {
+  k_row1<<<dim3(1), dim3(kRow1Threads), 0, st>>>(X, K, thr, O, counts, max_o, Xq, ldq, sx, Xo);
 }
 
 }  // namespace i8mm

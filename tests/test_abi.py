@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.i8mm_abi_version() == 8
+    assert L.i8mm_abi_version() == 9
     for code, name in [(0, b"I8MM_OK"), (1, b"I8MM_ERR_INVALID_ARG"), (2, b"I8MM_ERR_WORKSPACE"),
                        (3, b"I8MM_ERR_UNSUPPORTED"), (4, b"I8MM_ERR_HIP"),
                        (5, b"I8MM_ERR_OUTLIER_OVERFLOW")]:

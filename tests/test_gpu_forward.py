@@ -193,6 +193,111 @@ def test_one_to_four_tokens_fp16w_and_zeropoint(i8, T, K, N, planted):
     _zp_check(i8, d["X"], d["W"], d["bias"], 6.0, f"zero-point {T}x{K}x{N}")
 
 
+# One token, absmax layer: by default one launch of one workgroup takes
+# steps 1-2 for the row (no mask, no detection launch) and the product
+# gathers the weights of outlier sets wider than 128 columns itself; the
+# switch runs the detection and step-2 launches instead.  Both leave the
+# same bits in the workspace (Wo included), and the same Y for sets of up to
+# 128 columns.  Cases: K of one chunk a lane, an outlier in the last column
+# of a partial piece, K past one chunk round of the workgroup, the largest K
+# its registers take and one past it (the other launches), no outliers, a
+# set wider than 128 columns.
+@pytest.mark.parametrize("K,N,planted,thr", [
+    (16, 37, 1, 6.0), (1040, 70, 3, 6.0), (12304, 4099, 12, 6.0), (16384, 260, 40, 6.0),
+    (16400, 33, 5, 6.0), (2048, 90, 0, 6.0), (4096, 300, 0, 2.0),
+])
+def test_one_token_row_prep(i8, K, N, planted, thr):
+    d = make_random_case(K + 5 * N + planted, 1, K, N, n_planted=planted, bias=True)
+    X = d["X"].copy()
+    X[0, K - 1] = 9.0 if planted else X[0, K - 1]
+    runs = {}
+    try:
+        for on in (True, False):
+            i8.set_row_prep(on)
+            Y, _, _ = _full_check(i8, X, d["W"], d["bias"], thr, f"one token {K}x{N} row_prep={on}")
+            _, ws, _, _ = _run(i8, X, d["W"], d["bias"], thr)
+            runs[on] = (host(Y), _ws_views(i8, ws, 1, N, K, K))
+    finally:
+        i8.set_row_prep(True)
+    (Y1, v1), (Y3, v3) = runs[True], runs[False]
+    npad = ((int(v1["counts"][0]) + 31) // 32) * 32  # Xo / Wo columns written
+    for key in ("counts", "O", "sx", "Xq", "Xo", "Wo"):
+        a, b = v1[key], v3[key]
+        if key in ("Xo", "Wo"):
+            a, b = a[:, :npad], b[:, :npad]
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), key
+    if int(v1["counts"][0]) <= 128:
+        assert np.array_equal(Y1.view(np.uint16), Y3.view(np.uint16))
+
+
+def test_one_token_row_prep_overflow(i8):
+    # more outlier columns than max_outliers: the first max_outliers take the
+    # fp16 path, the rest are dropped, as with the other launches; the status
+    # says so
+    K, N, mo = 2048, 64, 40
+    d = make_random_case(5151, 1, K, N, n_planted=0, bias=False)
+    n = len(O.find_outliers(d["X"], 2.0))
+    assert n > mo
+    outs = {}
+    try:
+        for on in (True, False):
+            i8.set_row_prep(on)
+            Y, ws, _, _ = _run(i8, d["X"], d["W"], None, 2.0, max_outliers=mo)
+            code, nn = i8.linear_status(ws)
+            assert i8._lib.STATUS[code] == "I8MM_ERR_OUTLIER_OVERFLOW" and nn == n
+            outs[on] = (host(Y), _ws_views(i8, ws, 1, N, K, mo))
+    finally:
+        i8.set_row_prep(True)
+    (Y1, v1), (Y3, v3) = outs[True], outs[False]
+    npad = ((mo + 31) // 32) * 32
+    for key in ("O", "sx", "Xq"):
+        assert np.array_equal(v1[key].view(np.uint8), v3[key].view(np.uint8)), key
+    for key in ("Xo", "Wo"):
+        assert np.array_equal(v1[key][:, :npad].view(np.uint16), v3[key][:, :npad].view(np.uint16)), key
+    assert np.array_equal(Y1.view(np.uint16), Y3.view(np.uint16))
+
+
+def test_one_token_repeats_and_graph_replays(i8):
+    # calls in a row on one workspace (shapes alternating), and a captured
+    # graph replayed with other work in between, give the eager result
+    # every time
+    import torch
+    K, N = 4096, 1000
+    d = make_random_case(4242, 1, K, N, n_planted=6, bias=True)
+    d2 = make_random_case(4243, 1, 2048, 64, n_planted=2, bias=False)
+    Xd, Wd, bd = dev(d["X"]), dev(d["W"]), dev(d["bias"])
+    X2, W2 = dev(d2["X"]), dev(d2["W"])
+    CB, SCB = i8.quantize_weight(Wd)
+    CB2, SCB2 = i8.quantize_weight(W2)
+    ws = i8.alloc_workspace(1, N, K)
+    say("one token: repeated calls")
+    Yref = host(i8.linear_forward(Xd, CB, SCB, bd, 6.0, workspace=ws)).view(np.uint16)
+    Y2ref = host(i8.linear_forward(X2, CB2, SCB2, None, 6.0, workspace=ws)).view(np.uint16)
+    for _ in range(3):
+        assert np.array_equal(host(i8.linear_forward(Xd, CB, SCB, bd, 6.0, workspace=ws)).view(np.uint16), Yref)
+        assert np.array_equal(host(i8.linear_forward(X2, CB2, SCB2, None, 6.0, workspace=ws)).view(np.uint16), Y2ref)
+    say("one token: graph replays")
+    Y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        i8.linear_forward(Xd, CB, SCB, bd, 6.0, workspace=ws, out=Y)  # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        i8.linear_forward(Xd, CB, SCB, bd, 6.0, workspace=ws, out=Y)
+    for r in range(4):
+        Y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(Y).view(np.uint16), Yref), f"replay {r}"
+        # eager work on the same workspace between replays
+        assert np.array_equal(host(i8.linear_forward(X2, CB2, SCB2, None, 6.0, workspace=ws)).view(np.uint16), Y2ref)
+    code, n = i8.linear_status(ws)
+    assert code == 0
+
+
 def test_k_zero_gives_bias(i8):
     import torch
     T, N = 5, 7
