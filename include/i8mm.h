@@ -81,10 +81,10 @@ i8mm_status i8mm_set_split_override(int64_t splits);
 /*
  * Tuning and test control, process-wide: the output tile of the int8
  * product at T > 32 -- 0: 320 channels x 256 tokens, 1: 256 x 256, 2: 192 x
- * 256.  -1 (the default) lets the library choose per shape.  The tile does
+ * 256, 3: 320 x 128.  -1 (the default) lets the library choose per shape.  The tile does
  * not change Y: every element is computed with the same operations in the
  * same order.  Not synchronized with calls in flight on other host threads;
- * size workspaces under the same setting.  cfg < -1 or cfg > 2 ->
+ * size workspaces under the same setting.  cfg < -1 or cfg > 3 ->
  * I8MM_ERR_INVALID_ARG.
  */
 i8mm_status i8mm_set_tile_override(int64_t cfg);

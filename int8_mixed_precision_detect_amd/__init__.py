@@ -358,7 +358,7 @@ def gemm_s32(A: torch.Tensor, B: torch.Tensor, K: Optional[int] = None) -> torch
 
 def set_tile_override(cfg: int = -1) -> None:
     """Output tile of the product at T > 32 (0: 320 x 256, 1: 256 x 256,
-    2: 192 x 256); -1 = the library's choice.  Process-wide; size workspaces
+    2: 192 x 256, 3: 320 x 128); -1 = the library's choice.  Process-wide; size workspaces
     under the same setting."""
     check("i8mm_set_tile_override", lib().i8mm_set_tile_override(int(cfg)))
 

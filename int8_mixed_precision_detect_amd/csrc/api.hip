@@ -103,7 +103,7 @@ i8mm_status i8mm_set_row_prep(int enable) {
 }
 
 i8mm_status i8mm_set_tile_override(int64_t cfg) {
-  if (cfg < -1 || cfg > 2) return I8MM_ERR_INVALID_ARG;
+  if (cfg < -1 || cfg > 3) return I8MM_ERR_INVALID_ARG;
   set_tile_override(cfg);
   return I8MM_OK;
 }

@@ -765,8 +765,11 @@ std::atomic<int64_t> g_tile_override{-1};
 //   1: 256 x 256, 8 waves of 64 x 128, two 128-byte slices (128 KB LDS)
 //   2: 192 x 256, 8 waves of 48 x 128, two 128-byte slices (112 KB LDS):
 //      more tiles for narrow layers (N = 5120: 216 tiles instead of 160)
-constexpr int kCfgs = 3;
-constexpr int64_t kCfgBM[kCfgs] = {320, 256, 192}, kCfgBN[kCfgs] = {256, 256, 256};
+//   3: 320 x 128, 8 waves of 80 x 64, two 128-byte slices (112 KB LDS):
+//      narrow layers as exactly one tile a CU (N = 5120, T = 2048: 256
+//      tiles), without splitting K
+constexpr int kCfgs = 4;
+constexpr int64_t kCfgBM[kCfgs] = {320, 256, 192, 320}, kCfgBN[kCfgs] = {256, 256, 256, 128};
 constexpr int64_t kMaxSplits = 4;
 constexpr int64_t kMinSplitK = 1024;  // bytes of K a split walks at least
 
@@ -782,14 +785,19 @@ constexpr int64_t kMinSplitK = 1024;  // bytes of K a split walks at least
 // The constants are fitted to the measured durations of the three tiles on
 // MI355X over 21 shapes, T = 64-4096, K = 4096-20480, N = 4096-49152 and
 // 1-4 splits (least squares, then tuned so that the choice is the fastest
-// measured one: it is on 17 shapes, within 5.7 % on the other four).  So
-// the 13B first feed-forward layer (20480 x 2048 outputs, K = 5120) runs
-// 512 tiles of configuration 0 in two rounds, the down projection (5120 x
-// 2048, K = 20480) splits K in two over 128 of them, and the attention
-// projection (5120 x 2048, K = 5120) runs 216 tiles of configuration 2
-// unsplit.
-constexpr double kSliceUs[kCfgs] = {1.44, 1.45, 1.131}, kItemUs[kCfgs] = {16.44, 11.23, 10.85};
-constexpr double kFullRound[kCfgs] = {1.213, 1.123, 1.040};
+// measured one: it is on 17 shapes, within 5.7 % on the other four); the
+// 320 x 128 tile's, to its durations on 14 shapes measured beside the
+// others (its single-round shapes give 1.09 us a slice, 10.1 us of set-up
+// and 1.04-1.07 for a full round; over the 14 the planner's choices take
+// 0.8 % longer than the fastest measured ones, at most 7 % on one shape,
+// T = 512, K = N = 4096).  So the 13B first feed-forward layer (20480 x 2048
+// outputs, K = 5120) runs 512 tiles of configuration 0 in two rounds, the
+// down projection (5120 x 2048, K = 20480) splits K in two over 128 of
+// them, and the attention projection (5120 x 2048, K = 5120) runs 256
+// tiles of configuration 3, one a CU (57 us against 59 us for 216 of
+// configuration 2).
+constexpr double kSliceUs[kCfgs] = {1.44, 1.45, 1.131, 1.09}, kItemUs[kCfgs] = {16.44, 11.23, 10.85, 10.1};
+constexpr double kFullRound[kCfgs] = {1.213, 1.123, 1.040, 1.04};
 constexpr double kPartWriteUs = 0.0409, kPartReadUs = 0.0293;
 
 double plan_cost(int64_t T, int64_t N, int64_t K, int c, int64_t sp, int64_t cus) {
@@ -867,6 +875,10 @@ hipError_t launch_mode_z(const GemmArgs& a0, hipStream_t st) {
         e = launch_cfg<192, 256, 48, 128, 2, 128, MODE_PART>(a, st);
         return e != hipSuccess ? e : launch_cfg<192, 256, 48, 128, 2, 128, MODE_COMBINE, false, ZP>(c, st);
       }
+      if (cfg == 3) {
+        e = launch_cfg<320, 128, 80, 64, 2, 128, MODE_PART>(a, st);
+        return e != hipSuccess ? e : launch_cfg<320, 128, 80, 64, 2, 128, MODE_COMBINE, false, ZP>(c, st);
+      }
       e = launch_cfg<256, 256, 64, 128, 2, 128, MODE_PART>(a, st);
       return e != hipSuccess ? e
                              : launch_cfg<256, 256, 64, 128, 2, 128, MODE_COMBINE, false, ZP>(c, st);
@@ -874,6 +886,7 @@ hipError_t launch_mode_z(const GemmArgs& a0, hipStream_t st) {
   }
   if (cfg == 0) return launch_cfg<320, 256, 80, 128, 2, 128, MODE, false, ZP>(a, st);
   if (cfg == 2) return launch_cfg<192, 256, 48, 128, 2, 128, MODE, false, ZP>(a, st);
+  if (cfg == 3) return launch_cfg<320, 128, 80, 64, 2, 128, MODE, false, ZP>(a, st);
   return launch_cfg<256, 256, 64, 128, 2, 128, MODE, false, ZP>(a, st);
 }
 

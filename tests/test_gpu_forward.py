@@ -338,7 +338,8 @@ def test_split_k_is_bit_identical(i8, T, K, N, planted):
 @pytest.mark.parametrize("T,K,N,planted", [(600, 4112, 1000, 5), (2048, 1024, 5000, 40),
                                             (257, 520, 700, 3)])
 def test_tile_configs_are_bit_identical(i8, T, K, N, planted):
-    # the three wide tiles (320, 256, 192 channels x 256 tokens) compute each
+    # the four wide tiles (320, 256, 192 channels x 256 tokens, 320 x 128)
+    # compute each
     # element with the same operations in the same order: Y is the same bits,
     # unsplit and with K split in two; every one within the oracle's bound.
     # Ragged channel and token tiles; K = 4112 ends in a partial slice.
@@ -347,7 +348,7 @@ def test_tile_configs_are_bit_identical(i8, T, K, N, planted):
     try:
         for sp in (1, 2):
             i8.set_split_override(sp)
-            for cfg in (0, 1, 2):
+            for cfg in (0, 1, 2, 3):
                 i8.set_tile_override(cfg)
                 Y, _, _ = _full_check(i8, d["X"], d["W"], d["bias"], 6.0,
                                       f"tile {cfg} split {sp} {T}x{K}x{N}")
