@@ -87,7 +87,8 @@ def test_noalloc_matches_workspace_forward_on_shrinking_calls(i8):
     L = lib()
     d = make_inputs("13b")
     # full 13B first-FF shape, then a ragged small case with a bias, then a
-    # few-token case (the decode kernel path)
+    # few-token case (the decode kernel path), then one token (steps 1-2 in
+    # one workgroup's launch, counts written to the caller's status)
     n1 = _case(i8, L, d["X"], d["W"], d["bias"], d["threshold"], 256, "13b")
     assert n1 > 0
     c = make_random_case(11, 77, 1000, 300, n_planted=5)
@@ -96,6 +97,10 @@ def test_noalloc_matches_workspace_forward_on_shrinking_calls(i8):
     assert n2 >= 5
     c = make_random_case(12, 8, 512, 200, n_planted=3, bias=False)
     _case(i8, L, c["X"], c["W"], None, c["threshold"], 32, "decode 8x512x200", oracle=True)
+    c = make_random_case(15, 1, 2048, 130, n_planted=4, bias=True)
+    n4 = _case(i8, L, c["X"], c["W"], c["bias"], c["threshold"], 32, "one token 1x2048x130",
+               oracle=True)
+    assert n4 >= 4
 
 
 def test_noalloc_reports_overflow_and_rejects_oversize(i8):
