@@ -308,13 +308,54 @@ void launch_compact(const uint32_t* mask, int64_t K, int32_t* O, int32_t* counts
 // (they do not depend on it), so the two latencies overlap.  O is
 // ascending, so the gathers of consecutive o by consecutive lanes read
 // increasing addresses of one row; stores of Xo/Wo rows are coalesced.
-// Outlier sets beyond ocap fall back to enumerating the mask per row.
-// LDS: mask[KW], pref[KW + 1], O[ocap].
+// Wide sets (at least one column in 64, at most 4096) stream whole CB rows
+// through LDS instead of gathering, two rows in flight a workgroup; sets
+// beyond ocap fall back to enumerating the mask per row.
+// LDS: mask[KW], pref[KW + 1], O[ocap]; for the wide sets, two row buffers
+// over them.
 // ---------------------------------------------------------------------------
 constexpr int kChansPerWoBlock = 16;
 constexpr int64_t kFewChanGroups = 64;  // channel workgroups of a few-token call
 constexpr int kMaskWords = 2;  // mask words a thread requests before the row
-constexpr int kRowChunks = 4;  // 16-byte chunks of a CB row a thread streams (K <= 16384)
+constexpr int kRowChunks = 4;  // 4 KB pieces of a streamed CB row (K <= 16384)
+// Wide outlier sets of at most 256 * kWoRingCols columns: a thread keeps the
+// column of each of its outputs o = tid + 256 m in registers.
+constexpr int kWoRingCols = 16;
+// LDS of the step-2 kernel: mask[KW], pref[KW + 1], O[ocap], and at least
+// two CB rows rounded up to 4 KB plus a spare 1 KB where the wide-set Wo
+// build can run (16-byte multiples K <= 16384)
+constexpr size_t prep_lds_total(int64_t K, int64_t ocap) {
+  const size_t a = prep_lds_bytes(K, ocap);
+  const size_t b = K % 16 == 0 && K <= 256 * kRowChunks * 16
+                       ? (size_t)(2 * ((K + 4095) / 4096) * 4096 + 1024)
+                       : 0;
+  return a > b ? a : b;
+}
+// Eight signed bytes from LDS addresses a[0..7], read and waited for in one
+// asm block: the compiler's own wait before an LDS read, while loads into
+// LDS are in flight, covers all of them (it cannot tell the row buffers
+// apart) and would drain the loads of the rows after this one.
+__device__ __forceinline__ void lds_bytes8(const uint32_t (&a)[8], int (&c)[8]) {
+  asm volatile(
+      "ds_read_i8 %0, %8\n\t"
+      "ds_read_i8 %1, %9\n\t"
+      "ds_read_i8 %2, %10\n\t"
+      "ds_read_i8 %3, %11\n\t"
+      "ds_read_i8 %4, %12\n\t"
+      "ds_read_i8 %5, %13\n\t"
+      "ds_read_i8 %6, %14\n\t"
+      "ds_read_i8 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(c[4]), "=&v"(c[5]),
+        "=&v"(c[6]), "=&v"(c[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+}
+// wait until at most N of this wave's vector memory operations are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 // One row per workgroup measured best across the first-FF shapes (2 and 4
 // rows per workgroup: 13B-scale 12.2 / 10.9 us against 11.8 us, 175B-scale
 // 51 / 60 us against 46 us, 32-token decode 10 / 16 us against 7 us).
@@ -391,12 +432,13 @@ __global__ __launch_bounds__(256) void k_prep(
   const int64_t n_use = (int64_t)n_o < max_o ? n_o : max_o;
   const int64_t n_pad = round_up(n_use, 32);
   const bool listed = n_use <= ocap;
-  // Wide outlier sets touch nearly every cache line of a CB row: the channel
-  // workgroups then stream whole rows (through the LDS that would hold O)
-  // instead of gathering -- see below.
-  const bool wo_stream = !F16W && !ZP && !row_block && n_use * 64 >= K && K % 16 == 0 && K + 16 <= ocap * 4 &&
-                         K <= 256 * kRowChunks * 16 && (((uintptr_t)CB) & 15) == 0;
-  if (listed && !wo_stream) outlier_list<256>(smask, spref, KW, n_use, sO);
+  // Wide outlier sets (at least one column in 64, at most 256 * kWoRingCols
+  // of them) touch nearly every cache line of a CB row: the channel
+  // workgroups then stream whole rows instead of gathering -- see below.
+  const bool wo_ring = !F16W && !ZP && !row_block && n_use * 64 >= K && K % 16 == 0 &&
+                       K <= 256 * kRowChunks * 16 && (((uintptr_t)CB) & 15) == 0 && listed &&
+                       n_use <= 256 * kWoRingCols;
+  if (listed) outlier_list<256>(smask, spref, KW, n_use, sO);
   if (blockIdx.x == 0 && counts) {
     outlier_list<256>(smask, spref, KW, max_o, O_out);
     if (tid == 0) {
@@ -560,50 +602,105 @@ __global__ __launch_bounds__(256) void k_prep(
   // ---- dequantized outlier weight rows, blocks of 16 channels: block
   // blockIdx.x - nrowblk, then every (channel workgroups)-th one after it
   if (n_pad == 0 || n_use <= wo_skip) return;
+  if (wo_ring) {
+    // Rows streamed whole through two LDS row buffers (the mask, prefix and
+    // list are read before them and not after): row r + 2 is loaded straight
+    // into LDS, one 1 KB piece a wave and load, while row r is picked; each
+    // thread writes its outputs o = tid + 256 m of the row (coalesced) from
+    // the columns it holds.  Rows past the block load nothing (an empty
+    // buffer range reads 0), and pieces past K go to a spare 1 KB, so every
+    // row issues 4 loads and every pick 16 stores: the wait for row r counts
+    // the 20 issued after its loads.  (Its own loop: the other paths' loop
+    // invariants are not held in registers through it.)
+    uint32_t wcol[kWoRingCols / 2];  // two 16-bit columns a register (K <= 16384)
+#pragma unroll
+    for (int m = 0; m < kWoRingCols; m += 2) {
+      const int64_t o = tid + 256 * m;
+      const uint32_t c0 = o < n_use ? (uint32_t)sO[o] : 0u;
+      const uint32_t c1 = o + 256 < n_use ? (uint32_t)sO[o + 256] : 0u;
+      wcol[m / 2] = c0 | (c1 << 16);
+    }
+    __syncthreads();  // the row buffers overlay the list
+    const int64_t rbytes = round_up(K, (int64_t)4096);
+    char* lbase = (char*)sm;
+    char* spare = lbase + 2 * rbytes;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int64_t blk = (int64_t)blockIdx.x - nrowblk; blk < nwoblk;
+         blk += (int64_t)gridDim.x - nrowblk) {
+      const int64_t j0 = blk * kChansPerWoBlock;
+      const int64_t nch = min((int64_t)kChansPerWoBlock, N - j0);
+      auto load_row = [&](int64_t buf, int64_t r) {
+        const bool in = r < nch;
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(CB + (in ? (j0 + r) * K : 0), in ? (uint32_t)K : 0u);
+        int t = tid;
+        asm volatile("" : "+v"(t));
+#pragma unroll
+        for (int u = 0; u < kRowChunks; ++u) {
+          char* dst = 4096 * u < K ? lbase + buf * rbytes + 4096 * u + 1024 * wave : spare;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)dst, 16, (uint32_t)(t * 16 + 4096 * u),
+              0, 0, 0);
+        }
+      };
+      // (stores through a buffer range of the row's n_pad outputs: those
+      // past it, and all of a row outside the block, are dropped)
+      auto take_row = [&](int64_t buf, int64_t r) {
+        const bool in = r >= 0 && r < nch;
+        const int64_t j = j0 + (in ? r : 0);
+        const float sj = SCB[j];
+        const __amdgpu_buffer_rsrc_t rw =
+            make_rsrc(Wo + j * ldo, in ? (uint32_t)(n_pad * 2) : 0u);
+        const char* srow = lbase + buf * rbytes;
+        // (the thread index and packed columns made opaque here: the 16
+        // addresses, offsets and predicates derived from them are not
+        // hoisted out of the row loop into registers of their own)
+        int t = tid;
+        asm volatile("" : "+v"(t));
+#pragma unroll
+        for (int m = 0; m < kWoRingCols / 2; ++m) asm volatile("" : "+v"(wcol[m]));
+        const uint32_t lrow =
+            (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)srow;
+        // two batches of 8 outputs (LDS reads, then dequantize and store)
+#pragma unroll
+        for (int m0 = 0; m0 < kWoRingCols; m0 += 8) {
+          uint32_t ad[8];
+#pragma unroll
+          for (int m = 0; m < 8; ++m) ad[m] = lrow + ((wcol[(m0 + m) / 2] >> (16 * (m & 1))) & 0xffffu);
+          int code[8];
+          lds_bytes8(ad, code);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const int o = t + 256 * (m0 + m);
+            const unsigned short h =
+                __builtin_bit_cast(unsigned short, dequant_weight(code[m], sj));
+            __builtin_amdgcn_raw_buffer_store_b16(o < n_use ? h : (unsigned short)0, rw, o * 2,
+                                                  0, 0);
+          }
+        }
+      };
+      load_row(0, 0);
+      take_row(1, -1);
+      load_row(1, 1);
+      // (plain barriers: a workgroup fence would wait for every load into
+      // LDS in flight, the next row's too; the reads of a row are waited for
+      // where they are issued)
+      for (int64_t r = 0; r < nch; ++r) {
+        wait_vm<4 + 16>();             // this wave's pieces of row r are in LDS
+        __builtin_amdgcn_s_barrier();  // and every wave's
+        take_row(r & 1, r);
+        __builtin_amdgcn_s_barrier();  // the buffer is refilled next
+        load_row(r & 1, r + 2);
+      }
+    }
+    wait_vm<0>();  // no load into LDS outstanding when the workgroup ends
+    return;
+  }
   for (int64_t blk = (int64_t)blockIdx.x - nrowblk; blk < nwoblk;
        blk += (int64_t)gridDim.x - nrowblk) {
   const int64_t j0 = blk * kChansPerWoBlock;
   const int64_t nch = min((int64_t)kChansPerWoBlock, N - j0);
-  if (wo_stream) {
-    // Rows streamed whole: row r's 16-byte chunks go to LDS (coalesced
-    // loads), the next row's loads are in flight while this one's outlier
-    // bytes are picked by walking the mask words (output position from the
-    // prefix scan) and dequantized.
-    char* srow = (char*)sm + round_up((2 * KW + 1) * 4, 16);
-    const int64_t nck = K / 16;
-    v4i nx[kRowChunks];
-    auto load_row = [&](int64_t j) {
-#pragma unroll
-      for (int u = 0; u < kRowChunks; ++u) {
-        const int64_t c = tid + 256 * u;
-        nx[u] = c < nck ? *(const v4i*)(CB + j * K + 16 * c) : v4i{0, 0, 0, 0};
-      }
-    };
-    load_row(j0);
-    for (int64_t r = 0; r < nch; ++r) {
-      const int64_t j = j0 + r;
-#pragma unroll
-      for (int u = 0; u < kRowChunks; ++u) {
-        const int64_t c = tid + 256 * u;
-        if (c < nck) *(v4i*)(srow + 16 * c) = nx[u];
-      }
-      __syncthreads();
-      if (r + 1 < nch) load_row(j + 1);
-      const float sj = SCB[j];
-      _Float16* worow = Wo + j * ldo;
-      for (int64_t w = tid; w < KW; w += 256) {
-        uint32_t mb = smask[w];
-        int64_t o = spref[w];
-        while (mb && o < n_use) {
-          const int b = __ffs(mb) - 1;
-          mb &= mb - 1;
-          worow[o++] = dequant_weight(srow[w * 32 + b], sj);
-        }
-      }
-      for (int64_t o = n_use + tid; o < n_pad; o += 256) worow[o] = (_Float16)0.0f;
-      __syncthreads();  // the row buffer is rewritten next
-    }
-  } else if (listed) {
+  if (listed) {
     // per wave: items (channel r, chunk u of 64 outputs), wave-uniform, so
     // the channel's row address and scale stay scalar; a lane gathers
     // output o = 64u + lane; kGather items in flight
@@ -737,7 +834,7 @@ void launch_rowsum(const int8_t* CB, int64_t N, int64_t K, int32_t* rsum, hipStr
 
 template <bool VEC, int RPB, bool F16W, bool ZP>
 void launch_prep_t(const PrepArgs& p, dim3 g, size_t lds, int64_t nrowblk, hipStream_t st) {
-  (void)lds_limit<k_prep<VEC, RPB, F16W, ZP>>(prep_lds_bytes(kMaxK, kMaxOcap));
+  (void)lds_limit<k_prep<VEC, RPB, F16W, ZP>>(prep_lds_total(kMaxK, kMaxOcap));
   k_prep<VEC, RPB, F16W, ZP><<<g, dim3(256), lds, st>>>(
       p.X, p.T, p.K, p.mask, p.O_out, p.counts, p.max_o, p.Xq, p.ldq, p.sx, p.Xo, p.ldo, nrowblk,
       p.CB, p.SCB, p.N, p.Wo, p.ocap, p.wo_skip, p.W16, p.zp, p.osum,
@@ -754,7 +851,9 @@ void launch_prep(const PrepArgs& p, hipStream_t st) {
   // (only where the product can take the outliers itself: the fp16-weight
   // and zero-point layers always need Wo, and osum, from all blocks)
   if (p.T <= kFewT && p.wo_skip >= 0 && nwoblk > kFewChanGroups) nwoblk = kFewChanGroups;
-  const size_t lds = prep_lds_bytes(p.K, p.ocap);
+  // (the row buffers of the wide-set Wo build: absmax layer only)
+  const size_t lds =
+      p.W16 || p.zp ? prep_lds_bytes(p.K, p.ocap) : prep_lds_total(p.K, p.ocap);
   const dim3 g((unsigned)(nrowblk + nwoblk > 0 ? nrowblk + nwoblk : 1));
   if (p.W16) {
     if (p.vec)

@@ -440,6 +440,50 @@ def test_fp16_weight_variant_split_k(i8):
         i8.set_split_override(0)
 
 
+def test_fp16_weight_calls_and_graph_replays(i8):
+    # the per-call weight quantization on a non-default stream: calls in a
+    # row with another layer in between, and a captured graph replayed
+    # several times (CB zeroed before each), give the eager result
+    import torch
+    T, K, N = 96, 2048, 700
+    d = make_random_case(4711, T, K, N, n_planted=5, bias=True)
+    d2 = make_random_case(4712, T, K, 300, n_planted=3, bias=False)
+    Xd, Wd, bd = dev(d["X"]), dev(d["W"]), dev(d["bias"])
+    X2, W2 = dev(d2["X"]), dev(d2["W"])
+    s = torch.cuda.Stream()
+    ws = i8.alloc_workspace(T, N, K)
+    ws2 = i8.alloc_workspace(T, 300, K)
+    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
+    CB = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    SCB = torch.empty((N,), dtype=torch.float32, device="cuda")
+    say("fp16 weight: eager calls on a side stream, then graph replays")
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        i8.linear_forward_fp16w(Xd, Wd, bd, 6.0, workspace=ws, out=Y, CB=CB, SCB=SCB)
+        Yref, CBref, SCBref = host(Y).view(np.uint16), host(CB), host(SCB).view(np.uint32)
+        Y2ref = host(i8.linear_forward_fp16w(X2, W2, None, 6.0, workspace=ws2)[0]).view(np.uint16)
+        for _ in range(2):
+            CB.zero_()
+            i8.linear_forward_fp16w(Xd, Wd, bd, 6.0, workspace=ws, out=Y, CB=CB, SCB=SCB)
+            assert np.array_equal(host(Y).view(np.uint16), Yref)
+            assert np.array_equal(host(CB), CBref)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    Yo = O.linear_forward_fp16w(d["X"], d["W"], d["bias"], 6.0)
+    assert_y_close(Yref.view(np.float16), Yo, "fp16 weight, repeated calls")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        i8.linear_forward_fp16w(Xd, Wd, bd, 6.0, workspace=ws, out=Y, CB=CB, SCB=SCB)
+    for r in range(4):
+        Y.fill_(0)
+        CB.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(Y).view(np.uint16), Yref), f"replay {r}"
+        assert np.array_equal(host(CB), CBref) and np.array_equal(host(SCB).view(np.uint32), SCBref)
+        assert np.array_equal(host(i8.linear_forward_fp16w(X2, W2, None, 6.0, workspace=ws2)[0]).view(np.uint16), Y2ref)
+
+
 @pytest.mark.parametrize("N,K", [(7, 5), (300, 1024), (65, 1000), (1, 12288)])
 def test_weight_rowsum_exact(i8, N, K):
     rng = np.random.default_rng(N + K)

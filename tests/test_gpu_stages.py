@@ -169,6 +169,29 @@ def test_outlier_weights_bitexact(i8, case):
     assert np.all(Wo[:, n:npad].view(np.uint16) == 0)
 
 
+# Wide outlier sets (at least one column in 64): whole CB rows stream
+# through LDS, two rows in flight, when K is a multiple of 16 up to 16384 and
+# the set has at most 4096 columns; otherwise the gathers.  Cases: K not a
+# multiple of the 4 KB row piece, the largest set and one past it, the
+# largest K and one chunk past it, K not a multiple of 16, an odd number of
+# channels in the last block of 16, the smallest wide set.
+@pytest.mark.parametrize("N,K,n", [
+    (37, 5136, 1300), (300, 8192, 4096), (300, 8192, 4097), (19, 16384, 2000),
+    (40, 16400, 1000), (33, 1000, 200), (17, 4096, 64),
+])
+def test_outlier_weights_wide_sets(i8, N, K, n):
+    rng = np.random.default_rng(N * 31 + K + n)
+    W = make_weight(rng, N, K, 0.02)
+    Oo = np.sort(rng.choice(K, size=n, replace=False)).astype(np.int64)
+    CBo, SCBo = O.quantize_weight(W)
+    _, Woo = O.gather_outliers(np.zeros((1, K), np.float16), CBo, SCBo, Oo)
+    say("outlier_weights wide", N, K, n)
+    Wo = host(i8.outlier_weights(dev(CBo), dev(SCBo), dev(_mask_of(Oo, K)), K))
+    npad = ((n + 31) // 32) * 32
+    assert np.array_equal(Wo[:, :n].view(np.uint16), Woo.view(np.uint16))
+    assert np.all(Wo[:, n:npad].view(np.uint16) == 0)
+
+
 GEMM_SHAPES = [(16, 64, 64), (300, 517, 1024), (257, 300, 1000), (1, 1, 1), (5, 7, 24),
                (513, 257, 2048), (64, 1024, 4160), (2, 3, 12288),
                # large enough for the 320-channel tile (2 full waves of
