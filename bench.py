@@ -285,9 +285,10 @@ def main() -> int:
     # step 2 builds the outlier weights Wo unless the few-token tiles take
     # them from their own CB stream (int8 layer, T <= 32, n_o <= 128)
     wo_in_prep = T > 32 or n_o > 128 or args.layer != "int8"
-    # one token, absmax layer: steps 1-2 run as one launch of one workgroup
-    # (no mask, no Wo; the product gathers wide outlier sets from CB itself)
-    row_prep = T == 1 and args.layer == "int8" and K % 16 == 0 and K <= 16384
+    # one to eight tokens, absmax layer: steps 1-2 run as one launch of one
+    # workgroup (no mask, no Wo; the product takes every outlier set from CB
+    # itself)
+    row_prep = T <= 8 and args.layer == "int8" and K % 16 == 0 and K <= 16384
     if row_prep:
         wo_in_prep = False
     if T <= 32:

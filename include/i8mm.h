@@ -91,12 +91,12 @@ i8mm_status i8mm_set_tile_override(int64_t cfg);
 
 /*
  * Tuning and test control, process-wide: 1 (the default) takes steps 1-2
- * of a one-token forward of the absmax layer (T == 1, K a multiple of 16 up
- * to 16384, X 16-byte aligned; steps 1-2 of "LLM.int8() の核心アイデア")
- * from one launch of a single workgroup that holds the row -- with one row a
- * column is an outlier by its own value, so no mask and no detection
- * launch are needed -- and the product kernel gathers the weights of
- * outlier sets wider than 128 columns itself; 0 runs the detection and
+ * of a forward of one to eight tokens of the absmax layer (1 <= T <= 8, K a
+ * multiple of 16 up to 16384, X 16-byte aligned; steps 1-2 of "LLM.int8()
+ * の核心アイデア") from one launch of T workgroups, workgroup i holding row
+ * i -- each reads all T rows for the column flags, so no mask and no
+ * detection launch are needed -- and the product kernel takes the weights
+ * of outlier sets of any width out of CB itself; 0 runs the detection and
  * step-2 launches of every other call.  The workspace holds the same values
  * either way (the mask is not used), and so does Y for outlier sets of up
  * to 128 columns (wider sets sum their fp16 products in another order).

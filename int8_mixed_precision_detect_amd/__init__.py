@@ -364,8 +364,9 @@ def set_tile_override(cfg: int = -1) -> None:
 
 
 def set_row_prep(enable: bool = True) -> None:
-    """One-token forwards of the absmax layer take steps 1-2 from one launch
-    of one workgroup (the default) or from the detection and step-2 launches.
+    """Forwards of one to eight tokens of the absmax layer take steps 1-2
+    from one launch of a workgroup per row (the default) or from the
+    detection and step-2 launches.
     Process-wide; the workspace holds the same values either way, and Y too
     for outlier sets of up to 128 columns."""
     check("i8mm_set_row_prep", lib().i8mm_set_row_prep(1 if enable else 0))

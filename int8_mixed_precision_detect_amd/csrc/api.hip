@@ -68,7 +68,7 @@ std::atomic<bool> g_prof_on{false};
 int g_prof_n = 0;
 std::vector<hipEvent_t> g_prof_ev;  // kProfCap * 4 events, created on first enable
 
-// one-token forwards with steps 1-2 in one launch of one workgroup (see
+// forwards of one to eight tokens with steps 1-2 in one launch of one workgroup (see
 // i8mm_set_row_prep); a test and tuning control
 std::atomic<bool> g_row_prep{true};
 
@@ -253,14 +253,14 @@ i8mm_status forward_impl(const void* X, int64_t T, int64_t K, const int8_t* CB, 
   // Wo (and, zero-point, the outlier code sums) built by step 2: the
   // few-token tiles then do not rebuild Wo from CB
   a.wo_ready = W16 != nullptr || rsum != nullptr;
-  // One token, absmax layer, row-streaming product: steps 1-2 are one row,
-  // done by one workgroup in one launch (k_row1: no mask, no detection
-  // launch), and the product gathers the codes of wide outlier sets itself.
+  // One to eight tokens, absmax layer: steps 1-2 are done by one workgroup
+  // holding the rows, in one launch (k_rows: no mask, no detection launch),
+  // and the product takes the outlier weights of any set out of CB itself.
   // (In the stage profile, the detection stage covers both steps.)
-  if (T == 1 && xvec && K <= kRow1MaxK && fast && !a.wo_ready && gemv_supported(a) &&
+  if (T <= kRowsMaxT && xvec && K <= kRow1MaxK && fast && !a.wo_ready &&
       g_row_prep.load(std::memory_order_relaxed)) {
-    launch_row1((const _Float16*)X, K, threshold, O, counts, max_outliers, Xq, L.ldq, sx, Xo,
-                stream);
+    launch_rows((const _Float16*)X, T, K, threshold, O, counts, max_outliers, Xq, L.ldq, sx, Xo,
+                L.ldo, stream);
     if (ev) (void)hipEventRecord(ev[1], stream);
     if (ev) (void)hipEventRecord(ev[2], stream);
     a.wo_gather = true;

@@ -56,6 +56,7 @@ struct NoDma {
 };
 // LDS beyond the slices for MODE_FUSED_X: the outlier list and the tile's
 // X[:, O] values ([kFewOcap][BN] halves)
+static_assert((kFewOcap & (kFewOcap - 1)) == 0, "outlier staging: a power of two");
 constexpr size_t few_lds(int BN) { return (size_t)kFewOcap * 4 + (size_t)kFewOcap * BN * 2; }
 using I8Slices = std::false_type;
 using F16Slices = std::true_type;
@@ -306,7 +307,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   // last 64 columns of its Wo row held in registers, which goes to the
   // workspace after the K loop (and every 64th column for wider sets).  The
   // K loop loads and stores nothing in global memory but the slices: a store
-  // there, waited for with the slices, costs about a slice's time.
+  // there, waited for with the slices, costs about a slice's time.  Sets of
+  // up to kFewOcap columns are staged once; wider ones (when no step-2
+  // kernel built Wo) kFewOcap columns at a time, each restaging waiting for
+  // the slices in flight.
   int64_t n_use = 0;
   bool inloop = false;
   int64_t nxt = 0;
@@ -354,26 +358,35 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
         if (o0 + 8 * q < lim) *(v4u*)(dst + 8 * q) = v4u{wb[4 * q], wb[4 * q + 1], wb[4 * q + 2], wb[4 * q + 3]};
     }
   };
+  // columns o0 .. o0 + kFewOcap - 1 of O and of the tile's X[:, O] rows into
+  // sO / sXo (one wave: its LDS accesses stay in order)
+  auto stage_o = [&](int64_t o0) {
+    if constexpr (MODE == MODE_FUSED_X) {
+      const int64_t cnt = n_use - o0 < kFewOcap ? n_use - o0 : kFewOcap;
+      for (int64_t o = lane; o < cnt; o += 64) {
+        sO[o] = a.O[o0 + o];
+        // unconditional loads (rows clamped), so that they are all in flight at once
+        _Float16 xv[BN];
+#pragma unroll
+        for (int t = 0; t < BN; ++t) {
+          const int64_t tt = n0 + t < a.T ? n0 + t : a.T - 1;
+          xv[t] = a.Xo[tt * a.ldo + o0 + o];
+        }
+#pragma unroll
+        for (int t = 0; t < BN; ++t) sXo[o * BN + t] = n0 + t < a.T ? xv[t] : (_Float16)0.0f;
+      }
+    }
+  };
   // run while the first slices are in flight
   auto few_setup = [&]() {
     if constexpr (MODE == MODE_FUSED_X) {
       const int64_t n_o = a.counts[0];
       n_use = n_o < a.max_o ? n_o : a.max_o;
-      inloop = n_use <= kFewOcap && !a.wo_ready;
-      if (inloop) {
-        for (int64_t o = lane; o < n_use; o += 64) {
-          sO[o] = a.O[o];
-          // unconditional loads (rows clamped), so that they are all in flight at once
-          _Float16 xv[BN];
-#pragma unroll
-          for (int t = 0; t < BN; ++t) {
-            const int64_t tt = n0 + t < a.T ? n0 + t : a.T - 1;
-            xv[t] = a.Xo[tt * a.ldo + o];
-          }
-#pragma unroll
-          for (int t = 0; t < BN; ++t) sXo[o * BN + t] = n0 + t < a.T ? xv[t] : (_Float16)0.0f;
-        }
-      }
+      // sets built by no step-2 kernel (wo_gather: steps 1-2 were one
+      // workgroup) are walked whatever their width, kFewOcap columns of O
+      // and X[:, O] staged at a time
+      inloop = !a.wo_ready && (n_use <= kFewOcap || a.wo_gather);
+      if (inloop) stage_o(0);
       if (lane < BM && m0 + lane < a.N) sjx = a.SCB[m0 + lane];
       asm volatile("" ::"v"(sjx));  // waited for here rather than inside the K loop
       __syncthreads();
@@ -390,12 +403,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
         wb_push(__builtin_bit_cast(uint16_t, wo));
         if ((nxt & 63) == 63) wb_store(nxt - 63, n_use);
         const float wf = (float)wo;
-        const _Float16* xr = sXo + nxt * BN;
+        const _Float16* xr = sXo + (nxt & (kFewOcap - 1)) * BN;
 #pragma unroll
         for (int t = 0; t < PX; ++t) px[t] += (float)xr[t] * wf;
       }
       ++nxt;
-      nextc = nxt < n_use ? __builtin_amdgcn_readfirstlane(sO[nxt]) : 0x7fffffff;
+      if (nxt < n_use && (nxt & (kFewOcap - 1)) == 0) {
+        // the next kFewOcap columns (a wide set; its loads wait for the
+        // slices in flight too)
+        __syncthreads();
+        stage_o(nxt);
+        __syncthreads();
+      }
+      nextc = nxt < n_use ? __builtin_amdgcn_readfirstlane(sO[nxt & (kFewOcap - 1)]) : 0x7fffffff;
     }
   };
 

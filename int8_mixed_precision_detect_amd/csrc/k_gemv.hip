@@ -28,10 +28,10 @@
 // the codes give Wo (dequantized, written to the workspace) and the fp16
 // products sum_o X[t, o] Wo[j, o] in fp32, in increasing o.  Wider sets,
 // and the layers whose step 2 already built Wo, stream Wo and Xo through
-// the same loop with fp16 dot products instead -- except one-token calls
-// whose steps 1-2 ran as k_row1, which builds no Wo: their codes are
-// gathered from CB after the loop, 128 columns at a time, and summed the
-// same way as the extracted ones.
+// the same loop with fp16 dot products instead -- except calls whose steps
+// 1-2 ran as k_rows, which builds no Wo: their codes are gathered from CB
+// after the loop, 128 columns at a time, and summed the same way as the
+// extracted ones.
 //
 // Measured at 49152 x 12288 (HIP events around the product): 109 us at
 // T = 1 and 116 us at T = 4 against 124 us for the tiled few-token kernel;
@@ -249,10 +249,10 @@ __global__ __launch_bounds__(64) void k_gemv(GemmArgs a) {
     const float sj = valid ? a.SCB[f] : 0.0f;
     float y = (float)acc[0] * (sxt * (sj * (1.0f / 16129.0f)));
     const int64_t npad = round_up(n_use, 32);
-    // wider sets whose Wo no step-2 kernel built (wo_gather, one token):
-    // their codes are gathered from CB, kFewOcap columns at a time, and go
-    // the same way
-    const bool gather = FUSED && TT == 1 && a.wo_gather && !inloop && n_use > 0;
+    // wider sets whose Wo no step-2 kernel built (wo_gather: steps 1-2 were
+    // one workgroup): their codes are gathered from CB, kFewOcap columns at
+    // a time, and go the same way
+    const bool gather = FUSED && a.wo_gather && !inloop && n_use > 0;
     if (inloop || gather) {
       // Wo rows of this tile (zeros up to the 32-column pad), and the fp16
       // products in increasing o

@@ -5,11 +5,13 @@
 //   k_compact   mask -> ascending outlier list O and counts (stage entry)
 //   k_prep      outlier list from the mask, masked row absmax, int8 codes,
 //               X[:,O] gather, dequantized weight rows CB[:,O]*SCB/127
-//   k_row1      steps 1-2 of a single row (one-token calls) in one launch
+//   k_rows      steps 1-2 of up to 8 rows (one- to eight-token calls) in one launch
 //
 // The method: Hugging Face LLM.int8() summary (agentlenshq.com), section
 // "LLM.int8() の核心アイデア" steps 1-2; absmax rule from its section
 // "量子化の仕組み"; CB/SCB storage from "transformers への統合".
+#include <cstring>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -886,49 +888,75 @@ void launch_fill_bias(_Float16* Y, int64_t T, int64_t N, const _Float16* bias, i
 }
 
 // ---------------------------------------------------------------------------
-// Steps 1-2 for a single row of X (one-token calls) in one launch of one
-// workgroup: thread i holds chunks i + NT u (8 columns each) of the row in
-// registers, all requested at once.  With one row a column is an outlier
-// when its own |x| >= thr, so detection needs no mask: the flags, the
-// absmax over the other columns, the codes, the ascending list O (an
-// exclusive scan of the per-chunk counts in column order, one block-wide
-// scan per chunk round, skipped for rounds without outliers) and X[0, O]
-// are the values k_detect and k_prep produce for T = 1.  (One wave doing
-// it all took 21 us between events: its dependent VALU chains had nothing
-// to hide behind.)
+// Steps 1-2 for up to TR rows of X (one- to eight-token calls) in one launch:
+// workgroup i takes row i.  Thread t holds chunks t + NT u (8 columns each);
+// the column flags need every row, so each workgroup reads all T rows
+// (after the first, from L2) and ORs their flags, which for fp16 values is
+// an integer test: |x| >= thr exactly when the magnitude bits of x reach
+// those of the smallest fp16 value >= thr (`t16`, from the host), i.e. when
+// (bits & 0x7fff) + (0x8000 - t16) carries into bit 15 -- two operations a
+// pair of values, no conversion.  Every workgroup then has the same flags
+// and builds the same ascending list O (an exclusive scan of the per-chunk
+// counts in column order, one block-wide scan per chunk round); workgroup 0
+// publishes O and the counts, workgroup i writes X[i, O], the absmax of row
+// i over the other columns (a block max), its codes and sx[i] -- the values
+// k_detect and k_prep produce.  (One workgroup for all rows spent its time
+// in the codes of 8 x 12288 values: 24 us; one wave for one row, 21 us: its
+// dependent chains had nothing to hide behind.)
 // ---------------------------------------------------------------------------
-constexpr int kRow1Threads = 512;
-constexpr int kRow1Chunks = (int)(kRow1MaxK / 8 / kRow1Threads);  // chunks a thread, at most
-
-__global__ __launch_bounds__(kRow1Threads) void k_row1(
-    const _Float16* __restrict__ X, int64_t K, float thr, int32_t* __restrict__ O,
+template <int TR>
+__global__ __launch_bounds__(512) void k_rows(
+    const _Float16* __restrict__ X, int64_t T, int64_t K, uint32_t t16, int32_t* __restrict__ O,
     int32_t* __restrict__ counts, int64_t max_o, int8_t* __restrict__ Xq, int64_t ldq,
-    float* __restrict__ sx, _Float16* __restrict__ Xo_) {
+    float* __restrict__ sx, _Float16* __restrict__ Xo_, int64_t ldo) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NT = kRow1Threads, NW = NT / 64;
+  constexpr int NT = 512, NW = NT / 64, CH = (int)(kRow1MaxK / 8 / NT);
   __shared__ float red[NW];
-  __shared__ int32_t wtot[kRow1Chunks][NW];
+  __shared__ int32_t wtot[CH][NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
   const int64_t nc = K / 8;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)(K * 2));
-  v8h cv[kRow1Chunks];  // chunks past the row read 0
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)(T * K * 2));
+  // chunks past a row, and rows past T, read 0 (no flag)
+  auto load = [&](int64_t i, int u) {
+    const int64_t c = tid + NT * u;
+    return __builtin_bit_cast(
+        v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                 rx, (i < T && c < nc) ? (uint32_t)(i * K * 2 + c * 16) : 0x80000000u, 0, 0));
+  };
+  v4u own[CH], cv[TR][CH];
 #pragma unroll
-  for (int u = 0; u < kRow1Chunks; ++u)
-    cv[u] = __builtin_bit_cast(
-        v8h, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(tid + NT * u) * 16, 0, 0));
+  for (int u = 0; u < CH; ++u) own[u] = load(row, u);
+  if constexpr (TR > 1) {
+#pragma unroll
+    for (int i = 0; i < TR; ++i)
+#pragma unroll
+      for (int u = 0; u < CH; ++u) cv[i][u] = load(i, u);
+  }
+  const uint32_t addc = (0x8000u - t16) * 0x10001u;
+  auto carry = [&](const v4u& w, v4u& acc) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) acc[d] |= (w[d] & 0x7fff7fffu) + addc;
+  };
 
-  // flags and the absmax over the other columns; per round, the outlier
-  // count of each wave (for the scan)
-  uint32_t f[kRow1Chunks];
-  int incl[kRow1Chunks];
-  float m = 0.0f;
+  // flags of this thread's columns (any row); per round, the outlier count
+  // of each wave (for the scan)
+  uint32_t f[CH];
+  int incl[CH];
 #pragma unroll
-  for (int u = 0; u < kRow1Chunks; ++u) {
+  for (int u = 0; u < CH; ++u) {
+    v4u acc = v4u{0u, 0u, 0u, 0u};
+    if constexpr (TR > 1) {
+#pragma unroll
+      for (int i = 0; i < TR; ++i) carry(cv[i][u], acc);
+    } else {
+      carry(own[u], acc);
+    }
     uint32_t fu = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) fu |= (uint32_t)(fabsf(h2f(cv[u][e])) >= thr) << e;
+    for (int d = 0; d < 4; ++d)
+      fu |= ((acc[d] >> 15) & 1u) << (2 * d) | ((acc[d] >> 31) & 1u) << (2 * d + 1);
     f[u] = fu;
-    m = fmaxf(m, absmax8(zero_masked8(cv[u], fu)));
     const int cnt = __popc(fu);
     incl[u] = cnt;
 #pragma unroll
@@ -938,19 +966,14 @@ __global__ __launch_bounds__(kRow1Threads) void k_row1(
     }
     if (lane == 63) wtot[u][wave] = incl[u];
   }
-  m = wave_max(m);
-  if (lane == 0) red[wave] = m;
   __syncthreads();
-  float s = red[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) s = fmaxf(s, red[w]);
-  const float rs = code_recip(s);
 
-  // O (first max_o entries) and X[0, O]: columns in order are round-major
-  uint16_t* Xo = reinterpret_cast<uint16_t*>(Xo_);
+  // O (first max_o entries, workgroup 0) and X[row, O]: columns in order are
+  // round-major
+  uint16_t* Xo = reinterpret_cast<uint16_t*>(Xo_) + row * ldo;
   int n_o = 0;
 #pragma unroll
-  for (int u = 0; u < kRow1Chunks; ++u) {
+  for (int u = 0; u < CH; ++u) {
     int before = 0, total = 0;  // outliers of this round in lower waves, in all
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -959,14 +982,12 @@ __global__ __launch_bounds__(kRow1Threads) void k_row1(
       total += t;
     }
     if (f[u]) {
-      const v4u xw = __builtin_bit_cast(v4u, cv[u]);
-      const uint32_t w0 = xw[0], w1 = xw[1], w2 = xw[2], w3 = xw[3];
       int pos = n_o + before + incl[u] - __popc(f[u]);
       for (uint32_t ff = f[u]; ff; ff &= ff - 1, ++pos) {
         const int e = __builtin_ctz(ff);
         if (pos < max_o) {
-          const uint32_t wd = e < 2 ? w0 : e < 4 ? w1 : e < 6 ? w2 : w3;
-          O[pos] = (int32_t)((tid + NT * u) * 8 + e);
+          if (row == 0) O[pos] = (int32_t)((tid + NT * u) * 8 + e);
+          const uint32_t wd = own[u][e >> 1];
           Xo[pos] = (uint16_t)(wd >> (16 * (e & 1)));
         }
       }
@@ -976,27 +997,61 @@ __global__ __launch_bounds__(kRow1Threads) void k_row1(
   const int64_t n_use = n_o < max_o ? n_o : max_o;
   for (int64_t o = n_use + tid; o < round_up(n_use, 32); o += NT) Xo[o] = 0;
 
-  // codes, zeros on the outlier columns and past K
+  // the row's absmax over the other columns, its codes (zeros on the
+  // outlier columns and past K)
+  float m = 0.0f;
+  v8h xv[CH];
 #pragma unroll
-  for (int u = 0; u < kRow1Chunks; ++u) {
-    const int64_t c = tid + NT * u;
-    if (c < nc) *(v2u*)(Xq + c * 8) = absmax_codes8(zero_masked8(cv[u], f[u]), s, rs);
+  for (int u = 0; u < CH; ++u) {
+    xv[u] = zero_masked8(__builtin_bit_cast(v8h, own[u]), f[u]);
+    m = fmaxf(m, absmax8(xv[u]));
   }
-  for (int64_t k = K + 8 * tid; k < ldq; k += 8 * NT) *(v2u*)(Xq + k) = v2u{0u, 0u};
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  float sr = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) sr = fmaxf(sr, red[w]);
+  const float rs = code_recip(sr);
+  int8_t* q = Xq + row * ldq;
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int64_t c = tid + NT * u;
+    if (c < nc) *(v2u*)(q + c * 8) = absmax_codes8(xv[u], sr, rs);
+  }
+  for (int64_t k = K + 8 * tid; k < ldq; k += 8 * NT) *(v2u*)(q + k) = v2u{0u, 0u};
   if (tid == 0) {
-    sx[0] = s;
-    counts[0] = n_o;
-    counts[1] = n_o > max_o ? 1 : 0;
-    counts[2] = 0;
-    counts[3] = 0;
+    sx[row] = sr;
+    if (row == 0) {
+      counts[0] = n_o;
+      counts[1] = n_o > max_o ? 1 : 0;
+      counts[2] = 0;
+      counts[3] = 0;
+    }
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-void launch_row1(const _Float16* X, int64_t K, float thr, int32_t* O, int32_t* counts,
-                 int64_t max_o, int8_t* Xq, int64_t ldq, float* sx, _Float16* Xo,
+// The bits of the smallest fp16 value >= thr (thr > 0); above the largest
+// finite fp16 value, the bits of infinity (no finite value reaches it).
+static uint32_t fp16_ceil_bits(float thr) {
+  if (!(thr <= 65504.0f)) return 0x7C00u;
+  const _Float16 h = (_Float16)thr;  // round to nearest even
+  uint16_t b;
+  memcpy(&b, &h, 2);
+  if ((float)h < thr) b = (uint16_t)(b + 1);  // the next fp16 value up
+  return b;
+}
+
+void launch_rows(const _Float16* X, int64_t T, int64_t K, float thr, int32_t* O, int32_t* counts,
+                 int64_t max_o, int8_t* Xq, int64_t ldq, float* sx, _Float16* Xo, int64_t ldo,
                  hipStream_t st) {
-  k_row1<<<dim3(1), dim3(kRow1Threads), 0, st>>>(X, K, thr, O, counts, max_o, Xq, ldq, sx, Xo);
+  const uint32_t t16 = fp16_ceil_bits(thr);
+  if (T <= 1)
+    k_rows<1><<<dim3(1), dim3(512), 0, st>>>(X, T, K, t16, O, counts, max_o, Xq, ldq, sx, Xo, ldo);
+  else
+    k_rows<kRowsMaxT><<<dim3((unsigned)T), dim3(512), 0, st>>>(X, T, K, t16, O, counts, max_o,
+                                                               Xq, ldq, sx, Xo, ldo);
 }
 
 }  // namespace i8mm

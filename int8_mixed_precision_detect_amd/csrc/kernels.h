@@ -103,9 +103,8 @@ struct GemmArgs {
   const int32_t* zp;
   const int32_t* rsum;
   const int32_t* osum;
-  // Wo is not built for outlier sets wider than the row-streaming kernel
-  // picks out of CB itself (one-token calls, k_row1): that kernel gathers
-  // their codes from CB instead
+  // Wo is not built (steps 1-2 ran as k_rows): the few-token products take
+  // the codes of every outlier set from CB themselves, whatever its width
   bool wo_gather;
 };
 
@@ -143,13 +142,14 @@ constexpr int64_t kFewOcap = 128;
 // VALU dot products)
 bool gemv_supported(const GemmArgs& a);
 hipError_t launch_gemv(const GemmArgs& a, bool fused, hipStream_t st);
-// One row of X (T = 1, K % 8 == 0, K <= kRow1MaxK, 16-byte aligned): steps
-// 1-2 in one launch of one workgroup -- counts, O, sx, Xq (ldq) and Xo, the
-// same values k_detect + k_prep write (the mask is not used); Wo is left
-// to the row-streaming product (wo_gather).
+// Up to kRowsMaxT rows of X (1 <= T <= 8, K % 8 == 0, K <= kRow1MaxK,
+// 16-byte aligned): steps 1-2 in one launch of one workgroup -- counts, O,
+// sx, Xq (ldq) and Xo (ldo), the same values k_detect + k_prep write (the
+// mask is not used); Wo is left to the product (wo_gather).
 constexpr int64_t kRow1MaxK = 16384;
-void launch_row1(const _Float16* X, int64_t K, float thr, int32_t* O, int32_t* counts,
-                 int64_t max_o, int8_t* Xq, int64_t ldq, float* sx, _Float16* Xo,
+constexpr int kRowsMaxT = 8;
+void launch_rows(const _Float16* X, int64_t T, int64_t K, float thr, int32_t* O, int32_t* counts,
+                 int64_t max_o, int8_t* Xq, int64_t ldq, float* sx, _Float16* Xo, int64_t ldo,
                  hipStream_t st);
 
 }  // namespace i8mm

@@ -193,30 +193,47 @@ def test_one_to_four_tokens_fp16w_and_zeropoint(i8, T, K, N, planted):
     _zp_check(i8, d["X"], d["W"], d["bias"], 6.0, f"zero-point {T}x{K}x{N}")
 
 
-# One token, absmax layer: by default one launch of one workgroup takes
-# steps 1-2 for the row (no mask, no detection launch) and the product
-# gathers the weights of outlier sets wider than 128 columns itself; the
-# switch runs the detection and step-2 launches instead.  Both leave the
-# same bits in the workspace (Wo included), and the same Y for sets of up to
-# 128 columns.  Cases: K of one chunk a lane, an outlier in the last column
-# of a partial piece, K past one chunk round of the workgroup, the largest K
-# its registers take and one past it (the other launches), no outliers, a
-# set wider than 128 columns.
-@pytest.mark.parametrize("K,N,planted,thr", [
+# One to eight tokens, absmax layer: by default one launch of one workgroup
+# takes steps 1-2 for the rows (no mask, no detection launch) and the
+# product takes the weights of every outlier set out of CB itself (sets
+# wider than 128 columns too); the switch runs the detection and step-2
+# launches instead.  Both leave the same bits in the workspace (Wo
+# included), and the same Y for sets of up to 128 columns.  Cases: K of one
+# chunk a lane, an outlier in the last column of a partial piece, K past one
+# chunk round of the workgroup, the largest K its registers take and one
+# past it (the other launches), no outliers, a set wider than 128 columns;
+# one token, the row-streaming product (2-4 tokens) and the thin tiles (5-8).
+ROW_PREP_CASES = [
     (16, 37, 1, 6.0), (1040, 70, 3, 6.0), (12304, 4099, 12, 6.0), (16384, 260, 40, 6.0),
     (16400, 33, 5, 6.0), (2048, 90, 0, 6.0), (4096, 300, 0, 2.0),
+]
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+@pytest.mark.parametrize("K,N,planted,thr", ROW_PREP_CASES)
+def test_one_token_row_prep(i8, T, K, N, planted, thr):
+    _row_prep_case(i8, T, K, N, planted, thr)
+
+
+@pytest.mark.parametrize("T,K,N,planted,thr", [
+    (2, 1040, 70, 3, 6.0), (4, 4096, 300, 0, 2.0), (5, 12304, 4099, 12, 6.0), (6, 2048, 90, 0, 6.0),
+    (7, 4096, 300, 0, 2.0), (5, 16384, 260, 40, 6.0), (8, 4096, 33, 0, 1.0),
 ])
-def test_one_token_row_prep(i8, K, N, planted, thr):
-    d = make_random_case(K + 5 * N + planted, 1, K, N, n_planted=planted, bias=True)
+def test_few_tokens_row_prep(i8, T, K, N, planted, thr):
+    _row_prep_case(i8, T, K, N, planted, thr)
+
+
+def _row_prep_case(i8, T, K, N, planted, thr):
+    d = make_random_case(K + 5 * N + planted + 1000 * (T - 1), T, K, N, n_planted=planted, bias=True)
     X = d["X"].copy()
-    X[0, K - 1] = 9.0 if planted else X[0, K - 1]
+    X[T - 1, K - 1] = 9.0 if planted else X[T - 1, K - 1]
     runs = {}
     try:
         for on in (True, False):
             i8.set_row_prep(on)
-            Y, _, _ = _full_check(i8, X, d["W"], d["bias"], thr, f"one token {K}x{N} row_prep={on}")
+            Y, _, _ = _full_check(i8, X, d["W"], d["bias"], thr, f"{T} tokens {K}x{N} row_prep={on}")
             _, ws, _, _ = _run(i8, X, d["W"], d["bias"], thr)
-            runs[on] = (host(Y), _ws_views(i8, ws, 1, N, K, K))
+            runs[on] = (host(Y), _ws_views(i8, ws, T, N, K, K))
     finally:
         i8.set_row_prep(True)
     (Y1, v1), (Y3, v3) = runs[True], runs[False]
@@ -230,12 +247,13 @@ def test_one_token_row_prep(i8, K, N, planted, thr):
         assert np.array_equal(Y1.view(np.uint16), Y3.view(np.uint16))
 
 
-def test_one_token_row_prep_overflow(i8):
+@pytest.mark.parametrize("T", [1, 6])
+def test_one_token_row_prep_overflow(i8, T):
     # more outlier columns than max_outliers: the first max_outliers take the
     # fp16 path, the rest are dropped, as with the other launches; the status
     # says so
     K, N, mo = 2048, 64, 40
-    d = make_random_case(5151, 1, K, N, n_planted=0, bias=False)
+    d = make_random_case(5151 + T, T, K, N, n_planted=0, bias=False)
     n = len(O.find_outliers(d["X"], 2.0))
     assert n > mo
     outs = {}
@@ -245,7 +263,7 @@ def test_one_token_row_prep_overflow(i8):
             Y, ws, _, _ = _run(i8, d["X"], d["W"], None, 2.0, max_outliers=mo)
             code, nn = i8.linear_status(ws)
             assert i8._lib.STATUS[code] == "I8MM_ERR_OUTLIER_OVERFLOW" and nn == n
-            outs[on] = (host(Y), _ws_views(i8, ws, 1, N, K, mo))
+            outs[on] = (host(Y), _ws_views(i8, ws, T, N, K, mo))
     finally:
         i8.set_row_prep(True)
     (Y1, v1), (Y3, v3) = outs[True], outs[False]
@@ -257,27 +275,28 @@ def test_one_token_row_prep_overflow(i8):
     assert np.array_equal(Y1.view(np.uint16), Y3.view(np.uint16))
 
 
-def test_one_token_repeats_and_graph_replays(i8):
+@pytest.mark.parametrize("T", [1, 8])
+def test_one_token_repeats_and_graph_replays(i8, T):
     # calls in a row on one workspace (shapes alternating), and a captured
     # graph replayed with other work in between, give the eager result
     # every time
     import torch
     K, N = 4096, 1000
-    d = make_random_case(4242, 1, K, N, n_planted=6, bias=True)
-    d2 = make_random_case(4243, 1, 2048, 64, n_planted=2, bias=False)
+    d = make_random_case(4242, T, K, N, n_planted=6, bias=True)
+    d2 = make_random_case(4243, T, 2048, 64, n_planted=2, bias=False)
     Xd, Wd, bd = dev(d["X"]), dev(d["W"]), dev(d["bias"])
     X2, W2 = dev(d2["X"]), dev(d2["W"])
     CB, SCB = i8.quantize_weight(Wd)
     CB2, SCB2 = i8.quantize_weight(W2)
-    ws = i8.alloc_workspace(1, N, K)
-    say("one token: repeated calls")
+    ws = i8.alloc_workspace(T, N, K)
+    say("few tokens: repeated calls", T)
     Yref = host(i8.linear_forward(Xd, CB, SCB, bd, 6.0, workspace=ws)).view(np.uint16)
     Y2ref = host(i8.linear_forward(X2, CB2, SCB2, None, 6.0, workspace=ws)).view(np.uint16)
     for _ in range(3):
         assert np.array_equal(host(i8.linear_forward(Xd, CB, SCB, bd, 6.0, workspace=ws)).view(np.uint16), Yref)
         assert np.array_equal(host(i8.linear_forward(X2, CB2, SCB2, None, 6.0, workspace=ws)).view(np.uint16), Y2ref)
     say("one token: graph replays")
-    Y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+    Y = torch.empty((T, N), dtype=torch.float16, device="cuda")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):

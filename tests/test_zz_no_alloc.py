@@ -97,6 +97,8 @@ def test_noalloc_matches_workspace_forward_on_shrinking_calls(i8):
     assert n2 >= 5
     c = make_random_case(12, 8, 512, 200, n_planted=3, bias=False)
     _case(i8, L, c["X"], c["W"], None, c["threshold"], 32, "decode 8x512x200", oracle=True)
+    c = make_random_case(13, 20, 1024, 100, n_planted=3, bias=False)
+    _case(i8, L, c["X"], c["W"], None, c["threshold"], 32, "few tokens 20x1024x100", oracle=True)
     c = make_random_case(15, 1, 2048, 130, n_planted=4, bias=True)
     n4 = _case(i8, L, c["X"], c["W"], c["bias"], c["threshold"], 32, "one token 1x2048x130",
                oracle=True)
