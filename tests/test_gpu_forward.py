@@ -118,6 +118,34 @@ def test_zero_rows_and_threshold_tie(i8):
     _full_check(i8, X, W, d["bias"], 6.0, "zero rows / tie")
 
 
+@pytest.mark.parametrize("T", [1, 5, 8, 9])
+@pytest.mark.parametrize("thr", [6.0, 6.1, 5.999, 1e-4, 3e-8, 65504.0, 65505.0, float("inf")])
+def test_threshold_edges(i8, T, thr):
+    # Values on both sides of the threshold, for thresholds that fp16 holds
+    # exactly (6.0, 65504) and that it does not (6.1, 5.999, a subnormal
+    # one, one below the smallest fp16 value, one above the largest, +inf);
+    # T <= 8 takes steps 1-2 in one launch (an integer test on the fp16
+    # bits), T = 9 the detection launch (an fp32 compare): the same outliers
+    # as the oracle's fp32 test
+    K, N = 1024, 48
+    d = make_random_case(int(T * 1000 + 7), T, K, N, n_planted=0, bias=True)
+    scale = min(1e-5, thr / 1e3)  # the base values stay far below the threshold
+    X = (d["X"].astype(np.float64) * scale).astype(np.float16)
+    t32 = np.float32(thr)
+    h = np.float16(min(float(t32), 65504.0))
+    up = np.nextafter(h, np.float16(np.inf)) if h < np.float16(65504.0) else h
+    cands = [h, np.nextafter(h, np.float16(0)), up,
+             np.float16(6.0), np.float16(65504.0), np.float16(1e-4), np.float16(6e-8)]
+    cols = np.arange(0, K, K // (2 * len(cands)))[:2 * len(cands)]
+    for q, v in enumerate(cands):
+        if np.isfinite(v):
+            X[(q % T), cols[2 * q]] = v
+            X[((q + 1) % T), cols[2 * q + 1]] = -v
+    want = O.find_outliers(X, thr)
+    assert 0 < len(want) < 2 * len(cands) or (thr > 65504.0 and len(want) == 0)
+    _full_check(i8, X, d["W"], d["bias"], thr, f"{T} tokens, threshold {thr}")
+
+
 def test_wide_channel_tile(i8):
     # 2048 x 20380 outputs take the 320-channel tile configuration; the last
     # channel tile is ragged (220 of 320 rows)
