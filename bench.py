@@ -61,6 +61,7 @@ WORKLOAD_DESC = {
     "13b-down": "13b-scale second FF layer, down projection K = 4h (LLM.int8() linear)",
     "13b-attn": "13b-scale attention projection K = N = h (LLM.int8() linear)",
     "175b": "175b-scale first FF layer (LLM.int8() linear)",
+    "175b-n8": "175b-scale first FF layer, one GPU's 1/8 of the output channels (LLM.int8() linear)",
     "decode1": "decode1-scale first FF layer (LLM.int8() linear)",
     "decode8": "decode8-scale first FF layer (LLM.int8() linear)",
     "decode32": "decode32-scale first FF layer (LLM.int8() linear)",

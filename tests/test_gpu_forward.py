@@ -670,7 +670,7 @@ def test_full_size_workload_sampled(i8, name):
 
 
 @pytest.mark.parametrize("name", ["6.7b", "13b", "13b-down", "13b-attn", "decode1", "decode8",
-                                  "decode32", "175b"])
+                                  "decode32", "175b-n8", "175b"])
 def test_full_size_workload_every_output(i8, name):
     """All of Y at the workloads' full sizes against the oracle, over output
     channel blocks (the oracle sees every row and all of X for detection);

@@ -58,6 +58,10 @@ WORKLOADS = {
     "6.7b": Workload("6.7b", 2048, 4096, 16384, 1.0, 4, 6.0, 60.0, 0.2, 0.02, None),
     "13b": Workload("13b", 2048, 5120, 20480, 1.0, 6, 6.0, 60.0, 1.0, 0.02, 0.01),
     "175b": Workload("175b", 4096, 12288, 49152, 1.5, 12, 6.0, 80.0, 1.0, 0.015, None),
+    # one GPU's share of that layer under an 8-way split of the output
+    # channels: the same X, and (W drawn in row chunks from the same stream)
+    # exactly the first 6144 rows of its W
+    "175b-n8": Workload("175b-n8", 4096, 12288, 6144, 1.5, 12, 6.0, 80.0, 1.0, 0.015, None),
     # the rest of a 13B block: the second FF layer (down projection, K = 4h,
     # N = h) and an attention projection (K = N = h); same activation recipe
     "13b-down": Workload("13b-down", 2048, 20480, 5120, 1.0, 20, 6.0, 60.0, 1.0, 0.01, 0.01),
