@@ -55,9 +55,11 @@ struct NoDma {
   __device__ void operator()(int) const {}
 };
 // LDS beyond the slices for MODE_FUSED_X: the outlier list and the tile's
-// X[:, O] values ([kFewOcap][BN] halves)
-static_assert((kFewOcap & (kFewOcap - 1)) == 0, "outlier staging: a power of two");
-constexpr size_t few_lds(int BN) { return (size_t)kFewOcap * 4 + (size_t)kFewOcap * BN * 2; }
+// X[:, O] values ([kFewStage][BN] halves), kFewStage outlier columns at a
+// time: 48 rather than all kFewOcap the tiles take keeps 8 (32 x 16) or 4
+// (64 x 32) workgroups on a CU instead of 7 or 3
+constexpr int64_t kFewStage = 48;
+constexpr size_t few_lds(int BN) { return (size_t)kFewStage * 4 + (size_t)kFewStage * BN * 2; }
 using I8Slices = std::false_type;
 using F16Slices = std::true_type;
 
@@ -307,10 +309,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   // last 64 columns of its Wo row held in registers, which goes to the
   // workspace after the K loop (and every 64th column for wider sets).  The
   // K loop loads and stores nothing in global memory but the slices: a store
-  // there, waited for with the slices, costs about a slice's time.  Sets of
-  // up to kFewOcap columns are staged once; wider ones (when no step-2
-  // kernel built Wo) kFewOcap columns at a time, each restaging waiting for
-  // the slices in flight.
+  // there, waited for with the slices, costs about a slice's time.  O and
+  // X[:, O] are staged kFewStage columns at a time (sets up to kFewOcap
+  // columns, or any width when no step-2 kernel built Wo); each restaging
+  // waits for the slices in flight, which only sets wider than kFewStage
+  // columns pay.
   int64_t n_use = 0;
   bool inloop = false;
   int64_t nxt = 0;
@@ -320,8 +323,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
   float px[PX];
 #pragma unroll
   for (int t = 0; t < PX; ++t) px[t] = 0.0f;
-  int32_t* sO = (int32_t*)(lds + S * STAGE);                                   // [kFewOcap]
-  _Float16* sXo = (_Float16*)(lds + S * STAGE + kFewOcap * 4);                 // [kFewOcap][BN]
+  int32_t* sO = (int32_t*)(lds + S * STAGE);                                   // [kFewStage]
+  _Float16* sXo = (_Float16*)(lds + S * STAGE + kFewStage * 4);                // [kFewStage][BN]
+  int64_t sbase = 0;  // the first outlier column staged
   constexpr int WB = MODE == MODE_FUSED_X ? 32 : 1;  // dwords of the window
   uint32_t wb[WB];
 #pragma unroll
@@ -358,11 +362,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
         if (o0 + 8 * q < lim) *(v4u*)(dst + 8 * q) = v4u{wb[4 * q], wb[4 * q + 1], wb[4 * q + 2], wb[4 * q + 3]};
     }
   };
-  // columns o0 .. o0 + kFewOcap - 1 of O and of the tile's X[:, O] rows into
+  // columns o0 .. o0 + kFewStage - 1 of O and of the tile's X[:, O] rows into
   // sO / sXo (one wave: its LDS accesses stay in order)
   auto stage_o = [&](int64_t o0) {
     if constexpr (MODE == MODE_FUSED_X) {
-      const int64_t cnt = n_use - o0 < kFewOcap ? n_use - o0 : kFewOcap;
+      const int64_t cnt = n_use - o0 < kFewStage ? n_use - o0 : kFewStage;
       for (int64_t o = lane; o < cnt; o += 64) {
         sO[o] = a.O[o0 + o];
         // unconditional loads (rows clamped), so that they are all in flight at once
@@ -403,19 +407,20 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_i8(GemmArgs
         wb_push(__builtin_bit_cast(uint16_t, wo));
         if ((nxt & 63) == 63) wb_store(nxt - 63, n_use);
         const float wf = (float)wo;
-        const _Float16* xr = sXo + (nxt & (kFewOcap - 1)) * BN;
+        const _Float16* xr = sXo + (nxt - sbase) * BN;
 #pragma unroll
         for (int t = 0; t < PX; ++t) px[t] += (float)xr[t] * wf;
       }
       ++nxt;
-      if (nxt < n_use && (nxt & (kFewOcap - 1)) == 0) {
-        // the next kFewOcap columns (a wide set; its loads wait for the
-        // slices in flight too)
+      if (nxt < n_use && nxt - sbase == kFewStage) {
+        // the next kFewStage columns (its loads wait for the slices in
+        // flight too)
         __syncthreads();
         stage_o(nxt);
+        sbase = nxt;
         __syncthreads();
       }
-      nextc = nxt < n_use ? __builtin_amdgcn_readfirstlane(sO[nxt & (kFewOcap - 1)]) : 0x7fffffff;
+      nextc = nxt < n_use ? __builtin_amdgcn_readfirstlane(sO[nxt - sbase]) : 0x7fffffff;
     }
   };
 
