@@ -102,7 +102,7 @@ def test_modules_share_one_workspace_and_keep_scales_fp32(i8):
     mods = [i8.Int8Linear.from_linear(l).to("cuda").half() for l in lins]
     for m in mods:
         assert m.SCB.dtype == torch.float32 and m.CB.dtype == torch.int8
-    for rnd, T in enumerate([16, 3, 40, 1]):
+    for rnd, T in enumerate([16, 3, 40, 8, 1]):
         x = torch.randn(T, 64)
         x[:, 5] = 8.0
         h = x.to(torch.float16)
