@@ -713,16 +713,18 @@ def test_full_size_workload_every_output(i8, name):
     print(name, "n_o", n, "max err", worst)
 
 
-@pytest.mark.parametrize("layer", ["fp16w", "zeropoint"])
-def test_full_size_layer_variants(i8, layer):
-    """The fp16-weight and zero-point layers at the 13B first-FF shape they
-    are timed on: every output against the oracle, and their stage values
-    (CB, SCB, O, sx, Xq, Xo, Wo; Z and the outlier code sums) bit for bit."""
-    d = make_inputs("13b")
+@pytest.mark.parametrize("layer,name", [("fp16w", "13b"), ("zeropoint", "13b"),
+                                        ("zeropoint", "decode1"), ("fp16w", "decode8")])
+def test_full_size_layer_variants(i8, layer, name):
+    """The fp16-weight and zero-point layers at full workload sizes (the 13B
+    first-FF shape and the 175B-width decode shapes they are timed on): every
+    output against the oracle, and their stage values (CB, SCB, O, sx, Xq,
+    Xo, Wo; Z and the outlier code sums) bit for bit."""
+    d = make_inputs(name)
     if layer == "fp16w":
-        _fp16w_check(i8, d["X"], d["W"], d["bias"], d["threshold"], "13b fp16-weight layer")
+        _fp16w_check(i8, d["X"], d["W"], d["bias"], d["threshold"], f"{name} fp16-weight layer")
     else:
-        _zp_check(i8, d["X"], d["W"], d["bias"], d["threshold"], "13b zero-point layer")
+        _zp_check(i8, d["X"], d["W"], d["bias"], d["threshold"], f"{name} zero-point layer")
 
 
 @pytest.mark.parametrize("T", [8, 300])
